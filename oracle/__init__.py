@@ -1,0 +1,27 @@
+"""Float64 CPU oracle for the attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP product path
+never calls it, and this package never imports the product package: the two
+share no code.  Inputs reach both sides from ``workloads`` (seeded generators
+that hold no attention arithmetic).
+
+Two independent implementations of the same result:
+
+* ``naive.attention_naive`` / ``naive.attention_rows`` -- the plain definition
+  softmax(scale * Q K^T) V with an optional causal mask, two-pass stable
+  softmax over each full row, plus the per-row logsumexp L.
+* ``online.attention_online`` -- the blockwise online-softmax recurrence
+  (running row max m, running row sum l, rescale of the partial output when m
+  grows, one normalisation at the end), for any block sizes.
+
+The pages state the blockwise method reaches the identical (exact) result, so
+the two must agree to float64 rounding.  Pins: see ``tests/test_oracle_pins.py``.
+Every function here is pinned; none is "parity unpinned".
+"""
+
+from .naive import attention_naive, attention_rows
+from .online import attention_online
+from .compare import errors
+
+__all__ = ["attention_naive", "attention_rows", "attention_online", "errors"]
