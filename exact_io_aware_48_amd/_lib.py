@@ -1,0 +1,35 @@
+"""ctypes view of libfa_fwd.so: the C ABI declared in include/fa_fwd.h, nothing else."""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_HIP = range(7)
+FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+
+_lib = None
+
+
+def load():
+    """Load the in-tree library; raise loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_48_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, f32, f32, i32, vp]
+    lib.fa_fwd_fp8.restype = i32
+    pi, pl = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)
+    lib.fa_plan.argtypes = [i64, i64, i64, i64, i32, i32, pi, pi, pl, pi, pi, pl]
+    lib.fa_plan.restype = i32
+    lib.fa_status_string.argtypes = [i32]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i32
+    _lib = lib
+    return lib

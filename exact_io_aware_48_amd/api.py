@@ -1,0 +1,111 @@
+"""Python binding of the C ABI (include/fa_fwd.h), same names, argument marshalling only.
+
+torch supplies device memory and streams; every step of the attention forward
+runs in the HIP kernels of libfa_fwd.so.  There is no fallback: if the library
+is missing or a call fails, these functions raise.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+_DTYPE_CODE = {torch.float32: _lib.FA_F32, torch.bfloat16: _lib.FA_BF16}
+_FP8_DTYPES = (torch.float8_e4m3fn, torch.uint8)
+
+
+class FaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)}")
+
+
+def fa_status_string(status):
+    return _lib.load().fa_status_string(int(status)).decode()
+
+
+def fa_version():
+    return int(_lib.load().fa_version())
+
+
+def fa_plan(B, H, N, d, causal=False, dtype=_lib.FA_BF16):
+    """The launch fa_fwd would make (no GPU needed)."""
+    lib = _lib.load()
+    br, bc, thr, lds = (ctypes.c_int() for _ in range(4))
+    wg, tiles = ctypes.c_int64(), ctypes.c_int64()
+    st = lib.fa_plan(B, H, N, d, int(bool(causal)), int(dtype), ctypes.byref(br), ctypes.byref(bc),
+                     ctypes.byref(wg), ctypes.byref(thr), ctypes.byref(lds), ctypes.byref(tiles))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_plan")
+    return {"block_rows": br.value, "block_cols": bc.value, "workgroups": wg.value, "threads": thr.value,
+            "lds_bytes": lds.value, "kv_tiles": tiles.value}
+
+
+def _check(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fa_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None):
+    """O and per-row logsumexp of softmax(scale * Q K^T) V.
+
+    q, k, v: contiguous [B, H, N, d] device tensors, float32 or bfloat16
+    (float8_e4m3fn/uint8 bytes are taken with unit descales).  o, lse:
+    optional preallocated outputs ([B,H,N,d] of the input dtype -- bfloat16
+    for fp8 -- and float32 [B,H,N]).  Returns (o, lse).
+    """
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm)
+    if q.dtype in _FP8_DTYPES:
+        return fa_fwd_fp8(q, k, v, 1.0, 1.0, 1.0, o=o, lse=lse, scale=scale, causal=causal, stream=stream)
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"unsupported dtypes {q.dtype}/{k.dtype}/{v.dtype}")
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
+                            _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, scale=None, causal=False,
+               stream=None):
+    """FP8 (OCP e4m3fn) inputs with per-tensor descales; bfloat16 O, float32 lse."""
+    for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check(t, nm)
+        if t.dtype not in _FP8_DTYPES:
+            raise ValueError(f"{nm} must be float8_e4m3fn or uint8 bytes")
+    B, H, N, d = q8.shape
+    if k8.shape != q8.shape or v8.shape != q8.shape:
+        raise ValueError("q8, k8 and v8 must have the same shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, H, N, d, float(scale), float(q_descale), float(k_descale),
+                                float(v_descale), int(bool(causal)), _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_fp8")
+    return o, lse

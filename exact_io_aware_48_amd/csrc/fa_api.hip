@@ -1,0 +1,185 @@
+// C ABI of the FlashAttention forward library (declared in include/fa_fwd.h):
+// argument checks, choice of kernel instance, grid, launch.  No allocation,
+// no synchronisation, no state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <climits>
+
+#include "fa_fwd.h"
+#include "fa_fwd_kernel.hpp"
+
+namespace {
+
+using fa::Params;
+
+struct Tile {
+  int bc;      // keys per K/V tile
+  int nw;      // waves per workgroup (32 query rows each)
+  int lds;     // LDS bytes per workgroup
+};
+
+template <int D, int BC, int NW, int MODE>
+constexpr Tile tile_of() {
+  return Tile{BC, NW, fa::Geo<D, BC, NW, MODE>::LDSB};
+}
+
+// Tile shapes per (mode, d).  d = 256 with 16-bit tiles uses 32-key tiles so
+// that two workgroups (two waves per SIMD) fit in LDS and registers.
+template <int MODE, int D> struct Cfg;
+template <> struct Cfg<fa::MODE_BF16, 64> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_BF16, 128> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_BF16, 256> { static constexpr int BC = 32, NW = 4; };
+template <> struct Cfg<fa::MODE_FP8, 64> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_FP8, 128> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_FP8, 256> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_F32, 64> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_F32, 128> { static constexpr int BC = 64, NW = 4; };
+template <> struct Cfg<fa::MODE_F32, 256> { static constexpr int BC = 32, NW = 4; };
+
+template <int MODE, int D>
+Tile tile_for() {
+  return tile_of<D, Cfg<MODE, D>::BC, Cfg<MODE, D>::NW, MODE>();
+}
+
+Tile lookup_tile(int mode, int d) {
+  switch (mode) {
+    case fa::MODE_BF16: return d == 64 ? tile_for<fa::MODE_BF16, 64>() : d == 128 ? tile_for<fa::MODE_BF16, 128>() : tile_for<fa::MODE_BF16, 256>();
+    case fa::MODE_FP8: return d == 64 ? tile_for<fa::MODE_FP8, 64>() : d == 128 ? tile_for<fa::MODE_FP8, 128>() : tile_for<fa::MODE_FP8, 256>();
+    default: return d == 64 ? tile_for<fa::MODE_F32, 64>() : d == 128 ? tile_for<fa::MODE_F32, 128>() : tile_for<fa::MODE_F32, 256>();
+  }
+}
+
+template <int MODE, int D, bool CAUSAL>
+hipError_t launch(const Params& p, int grid, hipStream_t stream) {
+  constexpr int BC = Cfg<MODE, D>::BC, NW = Cfg<MODE, D>::NW;
+  Params args = p;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL>),
+                         dim3(grid), dim3(NW * 64), kargs, 0, stream);
+}
+
+template <int MODE>
+hipError_t dispatch_d(const Params& p, int d, bool causal, int grid, hipStream_t s) {
+  if (d == 64) return causal ? launch<MODE, 64, true>(p, grid, s) : launch<MODE, 64, false>(p, grid, s);
+  if (d == 128) return causal ? launch<MODE, 128, true>(p, grid, s) : launch<MODE, 128, false>(p, grid, s);
+  return causal ? launch<MODE, 256, true>(p, grid, s) : launch<MODE, 256, false>(p, grid, s);
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int mode_of(int dtype) {
+  return dtype == FA_BF16 ? fa::MODE_BF16 : dtype == FA_FP8_E4M3 ? fa::MODE_FP8 : fa::MODE_F32;
+}
+
+// shape and dtype checks shared by every entry point
+fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (B > INT_MAX / H) return FA_ERR_SHAPE;                 // B*H fits an int
+  if (N > (int64_t)INT_MAX / d) return FA_ERR_SHAPE;        // one head's elements fit an int
+  const int64_t bh = B * H;
+  if (bh > INT64_MAX / (N * d * 4)) return FA_ERR_SHAPE;    // byte sizes fit int64
+  const Tile t = lookup_tile(mode_of(dtype), (int)d);
+  const int64_t nrb = (N + 32 * t.nw - 1) / (32 * t.nw);
+  if (nrb * bh > INT_MAX) return FA_ERR_SHAPE;              // grid size
+  return FA_OK;
+}
+
+fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+              int64_t N, int64_t d, float scale, float dq, float dk, float dv, int causal, int dtype,
+              void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  fa_status st = check_shape(B, H, N, d, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  if (!(std::isfinite(dq) && dq > 0.f && std::isfinite(dk) && dk > 0.f && std::isfinite(dv) && dv > 0.f))
+    return FA_ERR_SCALE;
+  const int mode = mode_of(dtype);
+  const Tile t = lookup_tile(mode, (int)d);
+  const int br = 32 * t.nw;
+
+  Params p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+  p.BH = (int)(B * H);
+  p.N = (int)N;
+  p.nrb = (int)((N + br - 1) / br);
+  p.xcd_heads = (p.BH % 8 == 0) ? 1 : 0;
+  const double c2 = std::fabs((double)scale) * (double)dq * (double)dk * 1.4426950408889634;
+  if (!std::isfinite((float)c2)) return FA_ERR_SCALE;
+  p.c2 = (float)c2;
+  p.out_mul = mode == fa::MODE_FP8 ? dv / 256.f : 1.f;
+  p.qsign = 0;
+  if (scale < 0.f) p.qsign = mode == fa::MODE_BF16 ? 0x80008000u : mode == fa::MODE_FP8 ? 0x80808080u : 1u;
+
+  const int grid = p.nrb * p.BH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (mode) {
+    case fa::MODE_BF16: e = dispatch_d<fa::MODE_BF16>(p, (int)d, causal != 0, grid, s); break;
+    case fa::MODE_FP8: e = dispatch_d<fa::MODE_FP8>(p, (int)d, causal != 0, grid, s); break;
+    default: e = dispatch_d<fa::MODE_F32>(p, (int)d, causal != 0, grid, s); break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                 int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  return run(q, k, v, o, lse, B, H, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream);
+}
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int64_t B,
+                     int64_t H, int64_t N, int64_t d, float scale, float q_descale, float k_descale,
+                     float v_descale, int causal, void* stream) {
+  return run(q8, k8, v8, o_bf16, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, causal, FA_FP8_E4M3,
+             stream);
+}
+
+fa_status fa_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int dtype, int* block_rows,
+                  int* block_cols, int64_t* workgroups, int* threads, int* lds_bytes, int64_t* kv_tiles) {
+  fa_status st = check_shape(B, H, N, d, dtype);
+  if (st != FA_OK) return st;
+  const Tile t = lookup_tile(mode_of(dtype), (int)d);
+  const int64_t br = 32 * t.nw, bc = t.bc;
+  const int64_t nrb = (N + br - 1) / br, tiles_all = (N + bc - 1) / bc;
+  int64_t tiles = 0;
+  if (causal) {
+    for (int64_t rb = 0; rb < nrb; ++rb) {
+      const int64_t need = (rb * br + br - 1) / bc + 1;
+      tiles += need < tiles_all ? need : tiles_all;
+    }
+  } else {
+    tiles = nrb * tiles_all;
+  }
+  if (block_rows) *block_rows = (int)br;
+  if (block_cols) *block_cols = (int)bc;
+  if (workgroups) *workgroups = nrb * B * H;
+  if (threads) *threads = 64 * t.nw;
+  if (lds_bytes) *lds_bytes = t.lds;
+  if (kv_tiles) *kv_tiles = tiles * B * H;
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H, N must be >= 1 and sizes must fit the index types";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64, 128 or 256 and dtype a fa_dtype value";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and descales finite and > 0";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected the launch";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

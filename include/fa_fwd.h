@@ -1,0 +1,121 @@
+/*
+ * fa_fwd.h -- C ABI of the MI355X (gfx950) FlashAttention forward library.
+ *
+ * Operation.  For every batch b and head h, with S = scale * Q K^T (N x N):
+ *
+ *     O   = softmax(S) V                      (row-wise softmax)
+ *     lse = log(sum_j exp(S_ij))              (natural log, per query row i)
+ *
+ * optionally under the causal mask (query i sees key j iff j <= i).  This is
+ * the attention formula of the systems-analysis.info page "FlashAttention (PL)",
+ * section "Problematyka standardowego mechanizmu uwagi", and of the
+ * chipfoundryservices glossary entry "Flash Attention", "Standard attention"
+ * paragraph; ``scale`` is the 1/sqrt(d_k) factor.  The causal mask is the
+ * optional mask of the robocikowo.com "Flash Attention" page, and lse is the
+ * per-row logsumexp L that page says the backward pass recomputes from.
+ * The computation is tiled with an online softmax (glossary, "Tiling
+ * Algorithm" steps 1-6): the N x N score matrix never leaves the chip and the
+ * library needs no memory besides its arguments.
+ *
+ * Layout.  q, k, v and o are dense row-major [B][H][N][d] arrays (d fastest,
+ * no padding); lse is a dense [B][H][N] float array.  N is both the query and
+ * the key length.
+ *
+ * Memory and streams.  Every pointer is a device pointer owned by the caller;
+ * the library never allocates, frees, synchronises or keeps state between
+ * calls (all entry points are re-entrant).  ``stream`` is a hipStream_t
+ * (NULL = the default stream); the work is enqueued on it and the call
+ * returns without waiting.  o and lse must not overlap q, k, v or each other.
+ * Results are bitwise reproducible for equal inputs, shape and device.
+ *
+ * Errors.  Arguments are checked before anything is launched; on a failed
+ * check nothing is enqueued and the status says why.  A failure reported by
+ * the HIP runtime at launch returns FA_ERR_HIP.  Faults that happen while the
+ * kernel runs surface at the caller's next synchronisation, as with any HIP
+ * kernel.  Inputs are assumed finite.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or an element count overflows int64/int32 indexing */
+  FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128, 256}, or unknown dtype */
+  FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 5,       /* scale not finite, or an fp8 descale not finite and > 0 */
+  FA_ERR_HIP = 6          /* the HIP runtime rejected the launch */
+} fa_status;
+
+typedef enum {
+  FA_F32 = 0,       /* q, k, v, o are float32 (products use a three-term bf16 split) */
+  FA_BF16 = 1,      /* q, k, v, o are bfloat16 */
+  FA_FP8_E4M3 = 2   /* q, k, v are OCP e4m3fn bytes with unit descales; o is bfloat16 */
+} fa_dtype;
+
+/*
+ * fa_fwd -- exact attention forward, O and lse as described above.
+ *   q, k, v : inputs, element type given by dtype, [B][H][N][d]
+ *   o       : output, same element type as the inputs (bfloat16 for FA_FP8_E4M3)
+ *   lse     : output, float32 [B][H][N]
+ *   scale   : any finite value multiplying Q K^T (usually 1/sqrt(d))
+ *   causal  : 0 = no mask, nonzero = query i sees keys j <= i
+ *   dtype   : a fa_dtype value
+ *   stream  : hipStream_t to enqueue on
+ * FA_FP8_E4M3 here is fa_fwd_fp8 with all three descales equal to 1.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t N, int64_t d,
+                 float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- the same operation on FP8 inputs with per-tensor scales
+ * (the FP8 forward the pages attribute to FlashAttention-3: systems-analysis
+ * page section "FlashAttention-3 (2024)", glossary "Flash Attention 3
+ * (Hopper)" paragraph, dexblog.ro table row on data types).
+ *   q8, k8, v8 : OCP e4m3fn bytes [B][H][N][d]; the value of an element is
+ *                e4m3(x8) * x_descale
+ *   o_bf16     : bfloat16 output [B][H][N][d]
+ *   lse        : float32 [B][H][N], natural-log logsumexp of the scaled,
+ *                dequantised scores
+ *   *_descale  : finite and > 0, else FA_ERR_SCALE
+ * Softmax statistics and both products accumulate in float32.  The softmax
+ * probabilities are multiplied by 256 and rounded to e4m3 for the P V
+ * product; the factor is divided out in float32 and the row sum uses the
+ * unrounded probabilities.
+ */
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     float q_descale, float k_descale, float v_descale,
+                     int causal, void* stream);
+
+/*
+ * fa_plan -- the launch fa_fwd / fa_fwd_fp8 would make for this problem,
+ * without launching anything.  Any output pointer may be NULL.
+ *   block_rows / block_cols : queries per workgroup (B_r) and keys per K/V tile (B_c)
+ *   workgroups, threads     : grid size and threads per workgroup
+ *   lds_bytes               : LDS per workgroup
+ *   kv_tiles                : total K/V tiles the grid streams (fully masked causal tiles excluded)
+ * Returns the status fa_fwd would return for the same shape/dtype checks.
+ */
+fa_status fa_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int dtype,
+                  int* block_rows, int* block_cols, int64_t* workgroups, int* threads,
+                  int* lds_bytes, int64_t* kv_tiles);
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* fa_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

@@ -1,0 +1,102 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status before any
+HIP call.  No compute entry point is called with valid arguments here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_io_aware_48_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_io_aware_48_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_plan", "fa_status_string", "fa_version"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(lib._name)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in range(7):
+        s = lib.fa_status_string(code).decode()
+        assert s.startswith("FA_")
+    assert lib.fa_status_string(99).decode() == "unknown fa_status"
+    assert lib.fa_version() >= 100
+
+
+FAKE = 0x10000      # aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,expected", [
+    # q, k, v, o, lse, B, H, N, d, scale, causal, dtype
+    ((0, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0, 1), 1),
+    ((FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, 64, 0.1, 0, 1), 1),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 64, 64, 0.1, 0, 1), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 0, 64, 0.1, 0, 1), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, -3, 64, 64, 0.1, 0, 1), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 2**40, 64, 0.1, 0, 1), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2**31, 2**31, 64, 64, 0.1, 0, 1), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 96, 0.1, 0, 1), 3),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0, 7), 3),
+    ((FAKE + 2, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, 0, 1), 4),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE + 4, 1, 1, 64, 64, 0.1, 0, 1), 4),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, float("inf"), 0, 1), 5),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, float("nan"), 1, 0), 5),
+])
+def test_fa_fwd_validation(lib, args, expected):
+    assert lib.fa_fwd(*args, None) == expected
+
+
+@pytest.mark.parametrize("descales,expected", [((1.0, 0.0, 1.0), 5), ((-1.0, 1.0, 1.0), 5),
+                                                ((1.0, 1.0, float("nan")), 5), ((1.0, float("inf"), 1.0), 5)])
+def test_fa_fwd_fp8_descale_validation(lib, descales, expected):
+    assert lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, *descales, 0, None) == expected
+
+
+def test_fp8_scale_overflow_rejected(lib):
+    assert lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 1e30, 1e10, 1e10, 1.0, 0, None) == 5
+
+
+def test_plan_counts():
+    from exact_io_aware_48_amd import fa_plan, FA_BF16, FA_FP8_E4M3
+    p = fa_plan(1, 32, 8192, 128, causal=True, dtype=FA_BF16)
+    br, bc = p["block_rows"], p["block_cols"]
+    assert p["workgroups"] == 32 * 8192 // br
+    # causal: row block i streams ceil((i+1)*br/bc) tiles -- the blocks fully above the diagonal are skipped
+    per_head = sum(min(8192 // bc, ((i + 1) * br - 1) // bc + 1) for i in range(8192 // br))
+    assert p["kv_tiles"] == 32 * per_head
+    assert per_head < (8192 // br) * (8192 // bc) * 0.52
+    q = fa_plan(2, 8, 16384, 256, causal=False, dtype=FA_FP8_E4M3)
+    assert q["kv_tiles"] == 16 * (16384 // q["block_rows"]) * (16384 // q["block_cols"])
+    assert q["lds_bytes"] <= 160 * 1024
+    r = fa_plan(1, 1, 1, 64)
+    assert r["workgroups"] == 1 and r["kv_tiles"] == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    from exact_io_aware_48_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libfa_fwd.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

@@ -1,0 +1,182 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Inputs are the same seeded bytes on both sides (``workloads``).  Reduced-size
+cases are compared element by element over the whole output; they span
+several K/V tiles and query blocks and end on a ragged tail.  Full-size
+workloads are compared on every element where the oracle is cheap (the
+GPT-2- and BERT-shaped ones) and on sampled rows of sampled heads otherwise,
+in the same launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_rows, errors
+from workloads import WORKLOADS, by_name, make_inputs
+from workloads.gen import from_f32
+
+from gpu_util import TOL, check, oracle_full, run_gpu, sample_rows, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(*a):
+    print("CASE", *a, flush=True)
+
+
+# ---------------------------------------------------------------- reduced sizes, every element
+REDUCED = [
+    # (base workload, B, H, N)
+    ("tiny_f32_b1h2n256d64", 1, 2, 256),
+    ("tiny_f32_b1h2n256d64", 1, 1, 300),
+    ("gpt2s_causal_bf16_b8h12n1024d64", 2, 3, 333),
+    ("bertl_bf16_b16h16n512d64", 2, 2, 300),
+    ("long_causal_bf16_b1h32n8192d128", 1, 2, 1000),
+    ("wide_bf16_b2h8n16384d256", 1, 2, 700),
+    ("wide_fp8_b2h8n16384d256", 1, 2, 700),
+]
+
+
+@pytest.mark.parametrize("name,B,H,N", REDUCED)
+def test_reduced_workloads_all_elements(name, B, H, N):
+    w = by_name(name).with_(B=B, H=H, N=N)
+    _print_case(name, B, H, N)
+    x = make_inputs(w)
+    o, l = run_gpu(x)
+    o_ref, l_ref = oracle_full(x)
+    e = errors(o, o_ref, l, l_ref)
+    check(e, w.dtype, f"{name} B={B} H={H} N={N}")
+
+
+# ---------------------------------------------------------------- edge shapes
+EDGE = [(N, d, c, dt) for dt in ("bf16",) for d in (64, 128, 256) for N in (1, 7, 100, 257, 1000)
+        for c in (False, True)]
+EDGE += [(N, d, c, "f32") for d in (64, 128, 256) for N in (1, 100, 257) for c in (False, True)]
+EDGE += [(N, d, c, "fp8") for d in (64, 128, 256) for N in (1, 100, 257) for c in (False, True)]
+
+
+@pytest.mark.parametrize("N,d,causal,dtype", EDGE)
+def test_edge_shapes(N, d, causal, dtype):
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=2, N=N, d=d, causal=causal, dtype=dtype, seed=1000 + N + d)
+    _print_case("edge", N, d, causal, dtype)
+    x = make_inputs(w)
+    o, l = run_gpu(x)
+    o_ref, l_ref = oracle_full(x)
+    check(errors(o, o_ref, l, l_ref), dtype, f"edge N={N} d={d} causal={causal} {dtype}")
+
+
+# ---------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("name", [w.name for w in WORKLOADS])
+def test_full_size_workloads(name):
+    w = by_name(name)
+    _print_case("full", name)
+    x = make_inputs(w)
+    o, l = run_gpu(x)
+    if w.B * w.H * w.N * w.N * w.d <= 2**36:     # cheap enough: every element
+        o_ref, l_ref = oracle_full(x)
+        check(errors(o, o_ref, l, l_ref), w.dtype, name)
+        return
+    rng = np.random.default_rng(7)
+    heads = [(0, 0), (w.B - 1, w.H - 1)] + [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(2)]
+    og, orf, lg, lrf = [], [], [], []
+    for b, h in heads:
+        rows = sample_rows(w.N, seed=b * 131 + h)
+        r_o, r_l = attention_rows(x.f64("q", b, h), x.f64("k", b, h), x.f64("v", b, h), w.softmax_scale,
+                                  w.causal, rows)
+        og.append(o[b, h, rows]); orf.append(r_o); lg.append(l[b, h, rows]); lrf.append(r_l)
+    e = errors(np.concatenate(og), np.concatenate(orf), np.concatenate(lg), np.concatenate(lrf))
+    check(e, w.dtype, name + " (sampled rows)")
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+
+
+# ---------------------------------------------------------------- structured inputs
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 64), ("fp8", 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_v_all_ones(dtype, d, causal):
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=2, N=300, d=d, dtype=dtype, causal=causal)
+    base = make_inputs(w.with_(dtype="f32"))
+    x = from_f32(w, base.q * 2, base.k, np.ones_like(base.v))
+    _print_case("v_ones", dtype, d, causal)
+    o, _ = run_gpu(x)
+    # fp8: P is rounded to e4m3, whose half-ulp is 2**-4 of the value
+    tol = 2e-2 if dtype != "fp8" else 2.0**-4
+    assert np.max(np.abs(o - 1.0)) <= tol
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero_mean_and_log_count(dtype, d, causal):
+    N = 257
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=1, N=N, d=d, dtype=dtype, causal=causal)
+    base = make_inputs(w.with_(dtype="f32"))
+    x = from_f32(w, np.zeros_like(base.q), base.k, base.v)
+    _print_case("q_zero", dtype, d, causal)
+    o, l = run_gpu(x)
+    v = x.f64("v")[0, 0]
+    counts = np.arange(1, N + 1) if causal else np.full(N, N)
+    mean = np.cumsum(v, axis=0) / counts[:, None] if causal else np.broadcast_to(v.mean(axis=0), v.shape)
+    check(errors(o[0, 0], mean, l[0, 0], np.log(counts)), dtype, "q_zero")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_causal_row0_is_v0_bitwise(d):
+    w = by_name("gpt2s_causal_bf16_b8h12n1024d64").with_(B=1, H=2, N=200, d=d)
+    x = make_inputs(w)
+    _print_case("row0", d)
+    o, l = run_gpu(x)
+    assert np.array_equal(o[:, :, 0], x.f64("v")[:, :, 0])
+    s0 = w.softmax_scale * np.einsum("bhd,bhd->bh", x.f64("q")[:, :, 0], x.f64("k")[:, :, 0])
+    assert np.max(np.abs(l[:, :, 0] - s0)) < 1e-4
+
+
+def test_large_scores_from_shifted_keys():
+    # every key shifted by 16 in every dim: scores reach tens, so the running max moves a lot
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=1, N=320, d=64)
+    base = make_inputs(w.with_(dtype="f32"))
+    x = from_f32(w, base.q, base.k + np.float32(16.0), base.v)
+    _print_case("shift")
+    o, l = run_gpu(x)
+    ref, lref = oracle_full(x)
+    assert np.max(np.abs(lref)) > 20
+    check(errors(o, ref, l, lref), "bf16", "shifted keys")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
+def test_other_scales(scale):
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=2, N=190, d=64, causal=True)
+    x = make_inputs(w)
+    _print_case("scale", scale)
+    o, l = run_gpu(x, scale=scale)
+    ref, lref = oracle_full(x, scale=scale)
+    check(errors(o, ref, l, lref), "bf16", f"scale={scale}")
+
+
+# ---------------------------------------------------------------- runtime behaviour
+def test_deterministic_and_stream():
+    w = by_name("long_causal_bf16_b1h32n8192d128").with_(B=1, H=8, N=1500)
+    x = make_inputs(w)
+    _print_case("determinism")
+    a = run_gpu(x)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = run_gpu(x, stream=s)
+    c = run_gpu(x)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[0], c[0])
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[1], c[1])
+
+
+def test_error_paths_raise():
+    import exact_io_aware_48_amd as fa
+    q = torch.zeros((1, 1, 16, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd(q, q, q)
+    assert ei.value.status == 3
+    q = torch.zeros((1, 1, 16, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd(q, q, q, scale=float("inf"))
+    assert ei.value.status == 5
+    q8 = torch.zeros((1, 1, 16, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(fa.FaError) as ei:
+        fa.fa_fwd_fp8(q8, q8, q8, 1.0, 0.0, 1.0)
+    assert ei.value.status == 5
