@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention forward pass on one MI355X.
+
+A step is one call of the C-ABI entry point over one batch of the workload:
+the whole hot path (tile scheduling, Q/K/V loads, both MFMA products, online
+softmax, masking, normalisation, O and logsumexp stores) runs in that one
+kernel launch.  Inputs are seeded synthetic tensors (``workloads``) made
+resident in HBM before the timed region.
+
+Prints one JSON line.  ``value`` is whole-job throughput in TFLOP/s by the
+convention 4*B*H*N^2*d (halved for the causal mask) over the K timed steps on
+the host clock.  ``roofline.achieved`` is the same FLOP count per launch over
+the kernel's mean duration from HIP events recorded around every launch on
+the launch stream.  ``traffic`` is the HBM bytes per launch measured with
+rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same
+counters give for a plain copy of known size), read from profiles/ and only
+when the kernel sources are unchanged since that measurement.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
+    python bench.py --copy-calibration ...     also run a 256 MiB device copy (for PMC scaling)
+    python bench.py --summarize-pmc DIR_FETCH DIR_WRITE --workload NAME
+                                               write profiles/traffic_<NAME>.json from two PMC runs
+"""
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HEADLINE = "gpt2s_causal_bf16_b8h12n1024d64"
+METRIC = "attention fwd TFLOP/s and % of MI355X dense MFMA peak at N=1K–16K, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 2516.6, "fp8": 5033.2}   # dense MFMA peaks of the type the products use
+HBM_GBPS = 8000.0
+KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp", "exact_io_aware_48_amd/csrc/fa_api.hip"]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload_name):
+    path = os.path.join(PROFILES, f"traffic_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t["hbm_bytes_per_launch"]
+
+
+# ------------------------------------------------------------------ GPU timing
+def device_inputs(w):
+    import numpy as np
+    import torch
+    from workloads import make_inputs
+    x = make_inputs(w)
+    if w.dtype == "f32":
+        conv = lambda a: torch.from_numpy(a).cuda()
+    elif w.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        conv = lambda a: torch.from_numpy(a).cuda().view(torch.float8_e4m3fn)
+    return x, conv(x.q), conv(x.k), conv(x.v)
+
+
+def time_workload(w, steps, warmup):
+    import torch
+    import exact_io_aware_48_amd as fa
+    x, q, k, v = device_inputs(w)
+    out_dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=out_dtype, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    if w.dtype == "fp8":
+        launch = lambda: fa.fa_fwd_fp8(q, k, v, *x.descale, o=o, lse=lse, scale=w.softmax_scale,
+                                       causal=w.causal, stream=stream)
+    else:
+        launch = lambda: fa.fa_fwd(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal, stream=stream)
+    for _ in range(warmup):
+        launch()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {
+        "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
+        "kernel_ms_mean": sum(kms) / len(kms),
+        "kernel_ms_median": kms[len(kms) // 2],
+        "kernel_ms_p10": kms[len(kms) // 10],
+        "kernel_ms_p90": kms[(9 * len(kms)) // 10],
+    }
+
+
+def copy_calibration(nbytes=256 * 2**20, reps=3):
+    """A plain device copy of known size, so PMC byte counters can be scaled."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(w):
+    from oracle import attention_naive        # the float64 oracle, as it stands
+    from workloads import make_inputs
+    x = make_inputs(w)
+    threads = min(16, len(os.sched_getaffinity(0)))
+    q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
+    t0 = time.perf_counter()
+    attention_naive(q, k, v, w.softmax_scale, w.causal, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload ({w.B}x{w.H} heads, N={w.N}, d={w.d}, "
+                      f"{'causal' if w.causal else 'full'}) in float64 numpy, {dt:.2f} s wall; "
+                      f"FLOPs by the same convention as value"}
+
+
+# ------------------------------------------------------------------ PMC summary
+def _read_counter_csv(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def summarize_pmc(dir_fetch, dir_write, workload_name):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by a copy kernel."""
+    from workloads import by_name
+    w = by_name(workload_name)
+    out = {}
+    for counter, d in (("FETCH_SIZE", dir_fetch), ("WRITE_SIZE", dir_write)):
+        rows = [r for r in _read_counter_csv(d) if r.get("Counter_Name") == counter]
+        fa_vals = [float(r["Counter_Value"]) for r in rows if "fa_fwd_kernel" in r["Kernel_Name"]]
+        cp_vals = [float(r["Counter_Value"]) for r in rows if "fa_fwd_kernel" not in r["Kernel_Name"]
+                   and "opy" in r["Kernel_Name"]]
+        if not fa_vals:
+            raise SystemExit(f"no fa_fwd_kernel dispatch with {counter} in {d}")
+        copy_kib = max(cp_vals) if cp_vals else None
+        out[counter] = {"kib_per_dispatch_mean": sum(fa_vals) / len(fa_vals), "dispatches": len(fa_vals),
+                        "copy_kib": copy_kib}
+    known_kib = 256 * 1024.0                  # the calibration copy reads and writes 256 MiB
+    f_fetch = known_kib / out["FETCH_SIZE"]["copy_kib"] if out["FETCH_SIZE"]["copy_kib"] else 1.0
+    f_write = known_kib / out["WRITE_SIZE"]["copy_kib"] if out["WRITE_SIZE"]["copy_kib"] else 1.0
+    fetch_b = out["FETCH_SIZE"]["kib_per_dispatch_mean"] * 1024 * f_fetch
+    write_b = out["WRITE_SIZE"]["kib_per_dispatch_mean"] * 1024 * f_write
+    res = {
+        "workload": workload_name,
+        "kernel_source_sha": kernel_source_hash(),
+        "fetch_kib_per_dispatch": out["FETCH_SIZE"]["kib_per_dispatch_mean"],
+        "write_kib_per_dispatch": out["WRITE_SIZE"]["kib_per_dispatch_mean"],
+        "copy_scale_fetch": f_fetch,
+        "copy_scale_write": f_write,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "compulsory_bytes": w.compulsory_bytes,
+        "traffic_over_compulsory": (fetch_b + write_b) / w.compulsory_bytes,
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"traffic_{workload_name}.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
+# ------------------------------------------------------------------ main
+def line_for(w, t, steps, warmup):
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = w.flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    ai = w.flops / w.compulsory_bytes
+    return achieved, peak, ai
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return 0
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the attention forward shards over (batch, head) with no communication, so N GPUs would run "
+              "N independent copies of this kernel on 1/N of the heads", file=sys.stderr)
+        return 2
+
+    import torch
+    from workloads import WORKLOADS, by_name
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    w = by_name(args.workload)
+    if args.copy_calibration:
+        copy_calibration()
+    t = time_workload(w, args.steps, args.warmup)
+    achieved, peak, ai = line_for(w, t, args.steps, args.warmup)
+    value = w.flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
+    traffic = traffic_for(w.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["wall_ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q/K/V, resident in HBM before timing",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.softmax_scale, "parallelism": "single GPU"},
+        "pct_of_dense_peak": round(100 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_ms_mean": round(t["kernel_ms_mean"], 5),
+            "kernel_ms_p10_p50_p90": [round(t["kernel_ms_p10"], 5), round(t["kernel_ms_median"], 5),
+                                      round(t["kernel_ms_p90"], 5)],
+            "arith_intensity_flop_per_compulsory_byte": round(ai, 1),
+            "hbm_ceiling_tflops": round(min(peak, ai * HBM_GBPS / 1e3), 1),
+        },
+    }
+    if not args.only_headline:
+        others = {}
+        for ow in WORKLOADS:
+            if ow.name == w.name:
+                continue
+            ot = time_workload(ow, max(10, args.steps // 4), max(3, args.warmup // 2))
+            oa, opk, oai = line_for(ow, ot, 0, 0)
+            others[ow.name] = {"tflops_kernel": round(oa, 1), "pct_of_dense_peak": round(100 * oa / opk, 2),
+                               "kernel_ms_median": round(ot["kernel_ms_median"], 4), "dtype": ow.dtype,
+                               "peak": opk}
+        line["other_workloads"] = others
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -199,6 +199,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
   constexpr int NDB = D / 32;                       // 32-wide blocks of the head dim
   constexpr int QK_STEPS = MODE == MODE_FP8 ? D / 64 : D / 16;   // MFMA k-steps over d
   constexpr int PV_STEPS = MODE == MODE_FP8 ? BC / 64 : BC / 16; // MFMA k-steps over keys
+  // lazy-rescale threshold (log2 units); fp8 keeps P <= 1 so that 256 * P fits e4m3
+  constexpr float TAU = MODE == MODE_FP8 ? 0.f : 8.f;
 
   __shared__ __attribute__((aligned(16))) char smem_raw[G::LDSB];
   char FA_LDS* smem = (char FA_LDS*)(smem_raw);  // generic -> LDS address space
@@ -273,61 +275,79 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
     }
   }
 
-  // ---------------- K/V tile staging: HBM -> registers -> LDS
-  // thread t moves 16-byte LDS chunks u = t + i * NT of each plane
-  constexpr int SRC_VEC = MODE == MODE_F32 ? 2 : 1;   // 16-byte global loads per LDS chunk
-  i32x4 kst[G::UPT * SRC_VEC], vst[G::UPT * SRC_VEC];
+  // ---------------- K/V tile staging
+  // bf16/fp8: direct HBM -> LDS loads (global_load_lds_dwordx4).  One wave
+  // instruction fills 1 KiB of LDS, lane l at byte 16*l; the XOR swizzle is
+  // applied by choosing which global chunk each lane fetches.  Rows past the
+  // end of the sequence re-read row N-1: their scores are masked, so they
+  // only ever meet P = 0.
+  // fp32: HBM -> registers -> hi/lo split -> LDS, thread t moving the 16-byte
+  // LDS chunks u = t + i * NT of each plane.
+  constexpr bool DMA = MODE != MODE_F32;
+  constexpr int SRC_VEC = 2;                          // fp32: 16-byte global loads per LDS chunk
+  i32x4 kst[DMA ? 1 : G::UPT * SRC_VEC], vst[DMA ? 1 : G::UPT * SRC_VEC];
+  const char* kglob = static_cast<const char*>(p.k) + head_off * G::EB;
+  const char* vglob = static_cast<const char*>(p.v) + head_off * G::EB;
 
-  auto load_tile = [&](int j) {
+  auto issue_tile = [&](int j, int stage) {          // DMA modes
     const int row0 = j * BC;
+    char FA_LDS* kdst = smem + stage * G::STAGEB;
+    char FA_LDS* vdst = kdst + G::TILEB;
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
+      const int blk = (i * NW + wave) * 1024;         // this wave instruction's LDS block
+      const int off = blk + lane * 16;
+      const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
+      const int64_t grow = (int64_t)min(row0 + row, N - 1) * G::ROWB;
+      const char* ks = kglob + grow + ((pc ^ swz_k<D, BC, NW, MODE>(row)) << 4);
+      const char* vs = vglob + grow + ((pc ^ swz_v<D, BC, NW, MODE>(row)) << 4);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
+                                       (FA_LDS void*)(kdst + blk), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
+                                       (FA_LDS void*)(vdst + blk), 16, 0, 0);
+    }
+  };
+  auto load_tile = [&](int j) {                      // fp32 mode
+    const int row0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < (DMA ? 0 : G::UPT); ++i) {
       const int u = tid + i * G::NT;
       const int row = u / G::CPR, ch = u % G::CPR;
       const bool ok = row0 + row < N;
-      if constexpr (MODE == MODE_F32) {
-        const float* kb = static_cast<const float*>(p.k) + head_off + (int64_t)(row0 + row) * D + ch * 8;
-        const float* vb = static_cast<const float*>(p.v) + head_off + (int64_t)(row0 + row) * D + ch * 8;
-        kst[2 * i] = ok ? *reinterpret_cast<const i32x4*>(kb) : i32x4{0, 0, 0, 0};
-        kst[2 * i + 1] = ok ? *reinterpret_cast<const i32x4*>(kb + 4) : i32x4{0, 0, 0, 0};
-        vst[2 * i] = ok ? *reinterpret_cast<const i32x4*>(vb) : i32x4{0, 0, 0, 0};
-        vst[2 * i + 1] = ok ? *reinterpret_cast<const i32x4*>(vb + 4) : i32x4{0, 0, 0, 0};
-      } else {
-        const char* kb = static_cast<const char*>(p.k) + (head_off + (int64_t)(row0 + row) * D) * G::EB + ch * 16;
-        const char* vb = static_cast<const char*>(p.v) + (head_off + (int64_t)(row0 + row) * D) * G::EB + ch * 16;
-        kst[i] = ok ? *reinterpret_cast<const i32x4*>(kb) : i32x4{0, 0, 0, 0};
-        vst[i] = ok ? *reinterpret_cast<const i32x4*>(vb) : i32x4{0, 0, 0, 0};
-      }
+      const float* kb = static_cast<const float*>(p.k) + head_off + (int64_t)(row0 + row) * D + ch * 8;
+      const float* vb = static_cast<const float*>(p.v) + head_off + (int64_t)(row0 + row) * D + ch * 8;
+      kst[2 * i] = ok ? *reinterpret_cast<const i32x4*>(kb) : i32x4{0, 0, 0, 0};
+      kst[2 * i + 1] = ok ? *reinterpret_cast<const i32x4*>(kb + 4) : i32x4{0, 0, 0, 0};
+      vst[2 * i] = ok ? *reinterpret_cast<const i32x4*>(vb) : i32x4{0, 0, 0, 0};
+      vst[2 * i + 1] = ok ? *reinterpret_cast<const i32x4*>(vb + 4) : i32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](int stage) {                 // fp32 mode
     char FA_LDS* kbase = smem + stage * G::STAGEB;
     char FA_LDS* vbase = kbase + G::PLANES * G::TILEB;
 #pragma unroll
-    for (int i = 0; i < G::UPT; ++i) {
+    for (int i = 0; i < (DMA ? 0 : G::UPT); ++i) {
       const int u = tid + i * G::NT;
       const int row = u / G::CPR, ch = u % G::CPR;
       const int koff = row * G::ROWB + ((ch ^ swz_k<D, BC, NW, MODE>(row)) << 4);
       const int voff = row * G::ROWB + ((ch ^ swz_v<D, BC, NW, MODE>(row)) << 4);
-      if constexpr (MODE == MODE_F32) {
-        float kx[8], vx[8];
+      float kx[8], vx[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kx[e] = __int_as_float(kst[2 * i][e]); kx[4 + e] = __int_as_float(kst[2 * i + 1][e]);
-          vx[e] = __int_as_float(vst[2 * i][e]); vx[4 + e] = __int_as_float(vst[2 * i + 1][e]);
-        }
-        i32x4 kh, kl, vh, vl;
-        split8(kx, kh, kl);
-        split8(vx, vh, vl);
-        lds_write16(kbase + koff, kh);
-        lds_write16(kbase + G::TILEB + koff, kl);
-        lds_write16(vbase + voff, vh);
-        lds_write16(vbase + G::TILEB + voff, vl);
-      } else {
-        lds_write16(kbase + koff, kst[i]);
-        lds_write16(vbase + voff, vst[i]);
+      for (int e = 0; e < 4; ++e) {
+        kx[e] = __int_as_float(kst[2 * i][e]); kx[4 + e] = __int_as_float(kst[2 * i + 1][e]);
+        vx[e] = __int_as_float(vst[2 * i][e]); vx[4 + e] = __int_as_float(vst[2 * i + 1][e]);
       }
+      i32x4 kh, kl, vh, vl;
+      split8(kx, kh, kl);
+      split8(vx, vh, vl);
+      lds_write16(kbase + koff, kh);
+      lds_write16(kbase + G::TILEB + koff, kl);
+      lds_write16(vbase + voff, vh);
+      lds_write16(vbase + G::TILEB + voff, vl);
     }
+  };
+  auto wait_loads = [&]() {
+    if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
   // ---------------- running state
@@ -350,14 +370,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
     v_col_part = 2 * (16 * (grp & 1) + 4 * (lane & 3));
   }
 
-  load_tile(0);
-  store_tile(0);
+  if constexpr (DMA) {
+    issue_tile(0, 0);
+  } else {
+    load_tile(0);
+    store_tile(0);
+  }
+  wait_loads();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int stage = j & 1;
     const bool more = j + 1 < n_tiles;
-    if (more) load_tile(j + 1);
+    if (more) {
+      if constexpr (DMA) issue_tile(j + 1, stage ^ 1);
+      else load_tile(j + 1);
+    }
 
     if (j < wave_tiles) {
       const char FA_LDS* kbase = smem + stage * G::STAGEB;
@@ -412,10 +440,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[kb][i]);
       mraw = swap_halves_max(mraw);
-      const float m_new = fmaxf(m_run, mraw * c2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
+      // Rescale only when some row's maximum grew by more than TAU (log2
+      // units) over the base in use: exponents are then <= 2^TAU, and since O
+      // and l always share one base the result is the same.
+      const float m_tile = mraw * c2;
+      const bool grow = m_tile > m_run + TAU;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+        m_run = grow ? m_tile : m_run;
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
       float psum = 0.f;
 #pragma unroll
@@ -427,9 +464,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
           st[kb][i] = e;
           psum += e;
         }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+      l_run += psum;
 
       // ---- O^T += V_j^T P^T
       if constexpr (MODE == MODE_FP8) {
@@ -497,7 +532,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       }
     }
 
-    if (more) store_tile(stage ^ 1);
+    if constexpr (!DMA) {
+      if (more) store_tile(stage ^ 1);
+    }
+    wait_loads();
     __syncthreads();
   }
 
