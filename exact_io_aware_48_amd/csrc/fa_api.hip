@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <climits>
 
 #include "fa_fwd.h"
@@ -110,7 +111,10 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.xcd_heads = (p.BH % 8 == 0) ? 1 : 0;
   const double c2 = std::fabs((double)scale) * (double)dq * (double)dk * 1.4426950408889634;
   if (!std::isfinite((float)c2)) return FA_ERR_SCALE;
-  p.c2 = (float)c2;
+  // The kernel masks scores with -inf and relies on c2 > 0 to keep their
+  // exponentials at exactly 0.  For |scale| this small every product
+  // |score| * c2 is far below one fp32 ulp of 1, so flooring it changes nothing.
+  p.c2 = std::max((float)c2, 1e-30f);
   p.out_mul = mode == fa::MODE_FP8 ? dv / 256.f : 1.f;
   p.qsign = 0;
   if (scale < 0.f) p.qsign = mode == fa::MODE_BF16 ? 0x80008000u : mode == fa::MODE_FP8 ? 0x80808080u : 1u;

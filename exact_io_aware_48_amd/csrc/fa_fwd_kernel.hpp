@@ -142,6 +142,15 @@ __device__ __forceinline__ i32x4 lds_read16(const char FA_LDS* p) {
 __device__ __forceinline__ void lds_write16(char FA_LDS* p, i32x4 v) {
   *reinterpret_cast<i32x4 FA_LDS*>(p) = v;
 }
+// One 16-byte-per-lane HBM -> LDS load (global_load_lds_dwordx4): lane l's
+// 16 bytes land at LDS byte lds + 16*l.  Issued from asm so that the
+// compiler's wait insertion does not treat it as aliasing every later LDS read
+// (it cannot tell the stages apart); completion is awaited explicitly with
+// s_waitcnt vmcnt(0) before the workgroup barrier that publishes the tile.
+__device__ __forceinline__ void dma16(const void* gsrc, const char FA_LDS* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)lds;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0v) : "memory");
+}
 __device__ __forceinline__ i16x4 lds_tr16(const char FA_LDS* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4 FA_LDS*>(const_cast<char FA_LDS*>(p)));
 }
@@ -158,9 +167,10 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 }
 
 // round-to-nearest-even float -> bf16 bits (the hardware conversion)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(unsigned short, ha) | ((uint32_t)__builtin_bit_cast(unsigned short, hb) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));   // v_cvt_pk_bf16_f32
 }
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
   constexpr float TAU = MODE == MODE_FP8 ? 0.f : 8.f;
 
   __shared__ __attribute__((aligned(16))) char smem_raw[G::LDSB];
-  char FA_LDS* smem = (char FA_LDS*)(smem_raw);  // generic -> LDS address space
+  char FA_LDS* const smem = (char FA_LDS*)(smem_raw);  // generic -> LDS address space
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,9 +299,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
   const char* kglob = static_cast<const char*>(p.k) + head_off * G::EB;
   const char* vglob = static_cast<const char*>(p.v) + head_off * G::EB;
 
-  auto issue_tile = [&](int j, int stage) {          // DMA modes
+  auto issue_tile = [&](int j, char FA_LDS* kdst) __attribute__((always_inline)) {  // DMA modes
     const int row0 = j * BC;
-    char FA_LDS* kdst = smem + stage * G::STAGEB;
     char FA_LDS* vdst = kdst + G::TILEB;
 #pragma unroll
     for (int i = 0; i < G::UPT; ++i) {
@@ -301,13 +310,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       const int64_t grow = (int64_t)min(row0 + row, N - 1) * G::ROWB;
       const char* ks = kglob + grow + ((pc ^ swz_k<D, BC, NW, MODE>(row)) << 4);
       const char* vs = vglob + grow + ((pc ^ swz_v<D, BC, NW, MODE>(row)) << 4);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)ks,
-                                       (FA_LDS void*)(kdst + blk), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)vs,
-                                       (FA_LDS void*)(vdst + blk), 16, 0, 0);
+      dma16(ks, kdst + blk);
+      dma16(vs, vdst + blk);
     }
   };
-  auto load_tile = [&](int j) {                      // fp32 mode
+  auto load_tile = [&](int j) __attribute__((always_inline)) {                      // fp32 mode
     const int row0 = j * BC;
 #pragma unroll
     for (int i = 0; i < (DMA ? 0 : G::UPT); ++i) {
@@ -322,8 +329,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       vst[2 * i + 1] = ok ? *reinterpret_cast<const i32x4*>(vb + 4) : i32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&](int stage) {                 // fp32 mode
-    char FA_LDS* kbase = smem + stage * G::STAGEB;
+  auto store_tile = [&](char FA_LDS* kbase) __attribute__((always_inline)) {        // fp32 mode
     char FA_LDS* vbase = kbase + G::PLANES * G::TILEB;
 #pragma unroll
     for (int i = 0; i < (DMA ? 0 : G::UPT); ++i) {
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       lds_write16(vbase + G::TILEB + voff, vl);
     }
   };
-  auto wait_loads = [&]() {
+  auto wait_loads = [&]() __attribute__((always_inline)) {
     if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
@@ -356,7 +362,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
   for (int b = 0; b < NDB; ++b) oacc[b] = f32x16{};
   float m_run = -INFINITY;   // running max of scaled scores, log2 units (same in both lane halves)
   float l_run = 0.f;         // this lane half's part of the running sum
-  const float c2 = p.c2;
+  const float c2 = p.c2;     // > 0 (the host keeps it at least 1e-30)
+  // causal: the last key this lane's query sees, relative to 4*hf; ragged: the last key
+  const int last_key = (CAUSAL ? min(N - 1, my_q) : N - 1) - 4 * hf;
 
   // per-lane pieces of the V^T transpose-read addresses (see the PV step)
   const int grp = lane >> 4;              // 16-lane group
@@ -370,170 +378,167 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
     v_col_part = 2 * (16 * (grp & 1) + 4 * (lane & 3));
   }
 
+  auto compute_tile = [&](int j, const char FA_LDS* kbase) __attribute__((always_inline)) {
+    const char FA_LDS* vbase = kbase + G::PLANES * G::TILEB;
+
+    // ---- S^T = K_j Q^T   (rows: keys, columns: this wave's 32 queries)
+    f32x16 st[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < QK_STEPS; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row = 32 * kb + n;
+        if constexpr (MODE == MODE_FP8) {
+          const int sw = swz_k<D, BC, NW, MODE>(row);
+          const char FA_LDS* rp = kbase + row * G::ROWB;
+          i32x4 a0 = lds_read16(rp + (((4 * c + 2 * hf) ^ sw) << 4));
+          i32x4 a1 = lds_read16(rp + (((4 * c + 2 * hf + 1) ^ sw) << 4));
+          i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          st[kb] = mfma_fp8(a, q8[c], st[kb]);
+        } else {
+          const int off = row * G::ROWB + (((2 * c + hf) ^ swz_k<D, BC, NW, MODE>(row)) << 4);
+          bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kbase + off));
+          st[kb] = mfma_bf16(a, qa[c], st[kb]);
+          if constexpr (MODE == MODE_F32) {
+            bf16x8 al = __builtin_bit_cast(bf16x8, lds_read16(kbase + G::TILEB + off));
+            st[kb] = mfma_bf16(a, ql[c], st[kb]);
+            st[kb] = mfma_bf16(al, qa[c], st[kb]);
+          }
+        }
+      }
+    }
+
+    // ---- online softmax (log2 domain)
+    // accumulator element i of block kb holds key key0 + 32*kb + 8*(i/4) + 4*hf + i%4
+    const int key0 = j * BC;
+    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0)) {
+      const int lim = last_key - key0;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          st[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3)) > lim ? -INFINITY : st[kb][i];
+    }
+    float mraw = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[kb][i]);
+    mraw = swap_halves_max(mraw);
+    // Rescale only when some row's maximum grew by more than TAU (log2
+    // units) over the base in use: exponents are then <= 2^TAU, and since O
+    // and l always share one base the result is the same.
+    const float m_tile = mraw * c2;
+    const bool grow = m_tile > m_run + TAU;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+      m_run = grow ? m_tile : m_run;
+      l_run *= alpha;
+#pragma unroll
+      for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+
+    // masked scores are -inf and c2 > 0, so their exponentials are exactly 0
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i], c2, -m_use));
+        st[kb][i] = e;
+        psum += e;
+      }
+    l_run += psum;
+
+    // ---- O^T += V_j^T P^T
+    if constexpr (MODE == MODE_FP8) {
+#pragma unroll
+      for (int g = 0; g < PV_STEPS; ++g) {              // 64 keys per step
+        // B operand byte 16*kb' + i <- P of key 64g + 32*kb' + 8*(i/4) + 4*hf + i%4
+        i32x8 pb;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int kb = 2 * g + (w >> 2);
+          const int i0 = 4 * (w & 3);
+          int word = 0;
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][i0] * 256.f, st[kb][i0 + 1] * 256.f, word, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][i0 + 2] * 256.f, st[kb][i0 + 3] * 256.f, word, true);
+          pb[w] = word;
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          int va[8];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int row = 64 * g + 16 * t + v_row_part;
+            const int col = 32 * db + v_col_part;        // bytes
+            const int off = row * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row)) << 4) | (col & 15));
+            i32x2 r = lds_tr8(vbase + off);
+            va[2 * t] = r[0];
+            va[2 * t + 1] = r[1];
+          }
+          i32x8 a = i32x8{va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
+          oacc[db] = mfma_fp8(a, pb, oacc[db]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < PV_STEPS; ++s) {              // 16 keys per step
+        const int kb = s >> 1, cp = s & 1;
+        // B operand element i <- P of key 32*kb + 16*cp + 8*(i/4) + 4*hf + i%4
+        i32x4 ph, pl;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = st[kb][8 * cp + 2 * w], x1 = st[kb][8 * cp + 2 * w + 1];
+          const uint32_t h = pack_bf16x2(x0, x1);
+          ph[w] = (int)h;
+          if constexpr (MODE == MODE_F32)
+            pl[w] = (int)pack_bf16x2(x0 - bf16_lo_to_f32(h), x1 - bf16_hi_to_f32(h));
+        }
+        const bf16x8 pbh = __builtin_bit_cast(bf16x8, ph);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int row = 32 * kb + 16 * cp + v_row_part;
+          const int col = 32 * db * 2 + v_col_part;      // bytes
+          const int off0 = row * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row)) << 4) | (col & 15));
+          const int off1 = (row + 8) * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row + 8)) << 4) | (col & 15));
+          i16x4 lo = lds_tr16(vbase + off0), hi = lds_tr16(vbase + off1);
+          bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[db] = mfma_bf16(a, pbh, oacc[db]);
+          if constexpr (MODE == MODE_F32) {
+            i16x4 lo2 = lds_tr16(vbase + G::TILEB + off0), hi2 = lds_tr16(vbase + G::TILEB + off1);
+            bf16x8 al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+            oacc[db] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pl), oacc[db]);
+            oacc[db] = mfma_bf16(al, pbh, oacc[db]);
+          }
+        }
+      }
+    }
+  };
+
   if constexpr (DMA) {
-    issue_tile(0, 0);
+    issue_tile(0, smem);
   } else {
     load_tile(0);
-    store_tile(0);
+    store_tile(smem);
   }
   wait_loads();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
+    char FA_LDS* const cur = smem + (j & 1) * G::STAGEB;
+    char FA_LDS* const next = smem + ((j & 1) ^ 1) * G::STAGEB;
     const bool more = j + 1 < n_tiles;
-    if (more) {
-      if constexpr (DMA) issue_tile(j + 1, stage ^ 1);
+    if (more) {                       // start fetching tile j+1 into the other stage
+      if constexpr (DMA) issue_tile(j + 1, next);
       else load_tile(j + 1);
     }
-
-    if (j < wave_tiles) {
-      const char FA_LDS* kbase = smem + stage * G::STAGEB;
-      const char FA_LDS* vbase = kbase + G::PLANES * G::TILEB;
-
-      // ---- S^T = K_j Q^T   (rows: keys, columns: this wave's 32 queries)
-      f32x16 st[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < QK_STEPS; ++c) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int row = 32 * kb + n;
-          if constexpr (MODE == MODE_FP8) {
-            const int sw = swz_k<D, BC, NW, MODE>(row);
-            const char FA_LDS* rp = kbase + row * G::ROWB;
-            i32x4 a0 = lds_read16(rp + (((4 * c + 2 * hf) ^ sw) << 4));
-            i32x4 a1 = lds_read16(rp + (((4 * c + 2 * hf + 1) ^ sw) << 4));
-            i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            st[kb] = mfma_fp8(a, q8[c], st[kb]);
-          } else {
-            const int off = row * G::ROWB + (((2 * c + hf) ^ swz_k<D, BC, NW, MODE>(row)) << 4);
-            bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kbase + off));
-            st[kb] = mfma_bf16(a, qa[c], st[kb]);
-            if constexpr (MODE == MODE_F32) {
-              bf16x8 al = __builtin_bit_cast(bf16x8, lds_read16(kbase + G::TILEB + off));
-              st[kb] = mfma_bf16(a, ql[c], st[kb]);
-              st[kb] = mfma_bf16(al, qa[c], st[kb]);
-            }
-          }
-        }
-      }
-
-      // ---- online softmax (log2 domain)
-      // accumulator element i of block kb holds key 32*kb + 8*(i/4) + 4*hf + i%4
-      const int key0 = j * BC;
-      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0);
-      float mraw = -INFINITY;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool dead = key >= N || (CAUSAL && key > my_q);
-            st[kb][i] = dead ? -INFINITY : st[kb][i];
-          }
-      }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, st[kb][i]);
-      mraw = swap_halves_max(mraw);
-      // Rescale only when some row's maximum grew by more than TAU (log2
-      // units) over the base in use: exponents are then <= 2^TAU, and since O
-      // and l always share one base the result is the same.
-      const float m_tile = mraw * c2;
-      const bool grow = m_tile > m_run + TAU;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
-        m_run = grow ? m_tile : m_run;
-        l_run *= alpha;
-#pragma unroll
-        for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i], c2, -m_use));
-          if (need_mask) e = st[kb][i] == -INFINITY ? 0.f : e;
-          st[kb][i] = e;
-          psum += e;
-        }
-      l_run += psum;
-
-      // ---- O^T += V_j^T P^T
-      if constexpr (MODE == MODE_FP8) {
-#pragma unroll
-        for (int g = 0; g < PV_STEPS; ++g) {              // 64 keys per step
-          // B operand byte 16*kb' + i <- P of key 64g + 32*kb' + 8*(i/4) + 4*hf + i%4
-          i32x8 pb;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int kb = 2 * g + (w >> 2);
-            const int i0 = 4 * (w & 3);
-            int word = 0;
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][i0] * 256.f, st[kb][i0 + 1] * 256.f, word, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][i0 + 2] * 256.f, st[kb][i0 + 3] * 256.f, word, true);
-            pb[w] = word;
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            int va[8];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const int row = 64 * g + 16 * t + v_row_part;
-              const int col = 32 * db + v_col_part;        // bytes
-              const int off = row * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row)) << 4) | (col & 15));
-              i32x2 r = lds_tr8(vbase + off);
-              va[2 * t] = r[0];
-              va[2 * t + 1] = r[1];
-            }
-            i32x8 a = i32x8{va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
-            oacc[db] = mfma_fp8(a, pb, oacc[db]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < PV_STEPS; ++s) {              // 16 keys per step
-          const int kb = s >> 1, cp = s & 1;
-          // B operand element i <- P of key 32*kb + 16*cp + 8*(i/4) + 4*hf + i%4
-          i32x4 ph, pl;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float x0 = st[kb][8 * cp + 2 * w], x1 = st[kb][8 * cp + 2 * w + 1];
-            const uint32_t h = pack_bf16x2(x0, x1);
-            ph[w] = (int)h;
-            if constexpr (MODE == MODE_F32)
-              pl[w] = (int)pack_bf16x2(x0 - bf16_lo_to_f32(h), x1 - bf16_hi_to_f32(h));
-          }
-          const bf16x8 pbh = __builtin_bit_cast(bf16x8, ph);
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int row = 32 * kb + 16 * cp + v_row_part;
-            const int col = 32 * db * 2 + v_col_part;      // bytes
-            const int off0 = row * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row)) << 4) | (col & 15));
-            const int off1 = (row + 8) * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row + 8)) << 4) | (col & 15));
-            i16x4 lo = lds_tr16(vbase + off0), hi = lds_tr16(vbase + off1);
-            bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            oacc[db] = mfma_bf16(a, pbh, oacc[db]);
-            if constexpr (MODE == MODE_F32) {
-              i16x4 lo2 = lds_tr16(vbase + G::TILEB + off0), hi2 = lds_tr16(vbase + G::TILEB + off1);
-              bf16x8 al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
-              oacc[db] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pl), oacc[db]);
-              oacc[db] = mfma_bf16(al, pbh, oacc[db]);
-            }
-          }
-        }
-      }
-    }
-
+    if (j < wave_tiles) compute_tile(j, cur);
     if constexpr (!DMA) {
-      if (more) store_tile(stage ^ 1);
+      if (more) store_tile(next);
     }
     wait_loads();
     __syncthreads();
