@@ -15,49 +15,56 @@ namespace {
 
 using fa::Params;
 
+// A launch plan: tile shape and LDS footprint of the kernel instance used.
 struct Tile {
   int bc;      // keys per K/V tile
-  int nw;      // waves per workgroup (32 query rows each)
+  int nw;      // waves per workgroup, 32 query rows each
   int lds;     // LDS bytes per workgroup
+  int br() const { return 32 * nw; }
 };
 
-template <int D, int BC, int NW, int MODE>
-constexpr Tile tile_of() {
-  return Tile{BC, NW, fa::Geo<D, BC, NW, MODE>::LDSB};
-}
-
-// Tile shapes per (mode, d).  d = 256 with 16-bit tiles uses 32-key tiles so
-// that two workgroups (two waves per SIMD) fit in LDS and registers.
+// Shapes per (mode, d), chosen by measurement on MI355X.  Eight waves per
+// workgroup (256 query rows) halve the K/V traffic per FLOP for the large
+// heads; d = 64 keeps four waves so that the short causal rows spread over
+// more workgroups.  d = 256 with 16-bit tiles uses 32-key tiles to stay
+// within 256 VGPRs at two waves per SIMD.
 template <int MODE, int D> struct Cfg;
-template <> struct Cfg<fa::MODE_BF16, 64> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_BF16, 128> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_BF16, 256> { static constexpr int BC = 32, NW = 4; };
-template <> struct Cfg<fa::MODE_FP8, 64> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_FP8, 128> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_FP8, 256> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_F32, 64> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_F32, 128> { static constexpr int BC = 64, NW = 4; };
-template <> struct Cfg<fa::MODE_F32, 256> { static constexpr int BC = 32, NW = 4; };
+template <> struct Cfg<fa::MODE_BF16, 64> { static constexpr int BC = 64, NW = 4, ST = 2; };
+template <> struct Cfg<fa::MODE_BF16, 128> { static constexpr int BC = 128, NW = 8, ST = 2; };
+template <> struct Cfg<fa::MODE_BF16, 256> { static constexpr int BC = 32, NW = 8, ST = 2; };
+template <> struct Cfg<fa::MODE_FP8, 64> { static constexpr int BC = 64, NW = 4, ST = 2; };
+template <> struct Cfg<fa::MODE_FP8, 128> { static constexpr int BC = 64, NW = 8, ST = 2; };
+template <> struct Cfg<fa::MODE_FP8, 256> { static constexpr int BC = 64, NW = 8, ST = 2; };
+template <> struct Cfg<fa::MODE_F32, 64> { static constexpr int BC = 64, NW = 4, ST = 2; };
+template <> struct Cfg<fa::MODE_F32, 128> { static constexpr int BC = 64, NW = 4, ST = 2; };
+template <> struct Cfg<fa::MODE_F32, 256> { static constexpr int BC = 32, NW = 4, ST = 2; };
 
 template <int MODE, int D>
 Tile tile_for() {
-  return tile_of<D, Cfg<MODE, D>::BC, Cfg<MODE, D>::NW, MODE>();
+  constexpr int BC = Cfg<MODE, D>::BC, NW = Cfg<MODE, D>::NW, ST = Cfg<MODE, D>::ST;
+  return Tile{BC, NW, fa::Geo<D, BC, NW, MODE, ST>::LDSB};
 }
 
 Tile lookup_tile(int mode, int d) {
   switch (mode) {
-    case fa::MODE_BF16: return d == 64 ? tile_for<fa::MODE_BF16, 64>() : d == 128 ? tile_for<fa::MODE_BF16, 128>() : tile_for<fa::MODE_BF16, 256>();
-    case fa::MODE_FP8: return d == 64 ? tile_for<fa::MODE_FP8, 64>() : d == 128 ? tile_for<fa::MODE_FP8, 128>() : tile_for<fa::MODE_FP8, 256>();
-    default: return d == 64 ? tile_for<fa::MODE_F32, 64>() : d == 128 ? tile_for<fa::MODE_F32, 128>() : tile_for<fa::MODE_F32, 256>();
+    case fa::MODE_BF16:
+      return d == 64 ? tile_for<fa::MODE_BF16, 64>() : d == 128 ? tile_for<fa::MODE_BF16, 128>()
+                                                                 : tile_for<fa::MODE_BF16, 256>();
+    case fa::MODE_FP8:
+      return d == 64 ? tile_for<fa::MODE_FP8, 64>() : d == 128 ? tile_for<fa::MODE_FP8, 128>()
+                                                                : tile_for<fa::MODE_FP8, 256>();
+    default:
+      return d == 64 ? tile_for<fa::MODE_F32, 64>() : d == 128 ? tile_for<fa::MODE_F32, 128>()
+                                                                : tile_for<fa::MODE_F32, 256>();
   }
 }
 
 template <int MODE, int D, bool CAUSAL>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
-  constexpr int BC = Cfg<MODE, D>::BC, NW = Cfg<MODE, D>::NW;
+  constexpr int BC = Cfg<MODE, D>::BC, NW = Cfg<MODE, D>::NW, ST = Cfg<MODE, D>::ST;
   Params args = p;
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL>),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, ST>),
                          dim3(grid), dim3(NW * 64), kargs, 0, stream);
 }
 
@@ -84,7 +91,7 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
   const int64_t bh = B * H;
   if (bh > INT64_MAX / (N * d * 4)) return FA_ERR_SHAPE;    // byte sizes fit int64
   const Tile t = lookup_tile(mode_of(dtype), (int)d);
-  const int64_t nrb = (N + 32 * t.nw - 1) / (32 * t.nw);
+  const int64_t nrb = (N + t.br() - 1) / t.br();
   if (nrb * bh > INT_MAX) return FA_ERR_SHAPE;              // grid size
   return FA_OK;
 }
@@ -101,7 +108,7 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
     return FA_ERR_SCALE;
   const int mode = mode_of(dtype);
   const Tile t = lookup_tile(mode, (int)d);
-  const int br = 32 * t.nw;
+  const int br = t.br();
 
   Params p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
@@ -151,7 +158,7 @@ fa_status fa_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int dt
   fa_status st = check_shape(B, H, N, d, dtype);
   if (st != FA_OK) return st;
   const Tile t = lookup_tile(mode_of(dtype), (int)d);
-  const int64_t br = 32 * t.nw, bc = t.bc;
+  const int64_t br = t.br(), bc = t.bc;
   const int64_t nrb = (N + br - 1) / br, tiles_all = (N + bc - 1) / bc;
   int64_t tiles = 0;
   if (causal) {

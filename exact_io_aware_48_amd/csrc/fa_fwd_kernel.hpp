@@ -43,168 +43,15 @@
 //               lo = bf16(x - hi) and each product uses hi*hi + hi*lo + lo*hi.
 #pragma once
 
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "fa_common.hpp"
 
 namespace fa {
 
-enum { MODE_BF16 = 0, MODE_FP8 = 1, MODE_F32 = 2 };
-
-struct Params {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* o;
-  float* lse;
-  int BH;          // batch * heads
-  int N;           // sequence length (queries = keys)
-  int nrb;         // row blocks per head = ceil(N / B_r)
-  int xcd_heads;   // 1: heads are spread over XCDs head-major (BH % 8 == 0)
-  float c2;        // |scale| * descale_q * descale_k * log2(e)
-  float out_mul;   // factor applied to O before dividing by l (fp8: descale_v / 256)
-  uint32_t qsign;  // XOR mask on Q's sign bits (negative scale)
-};
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
-
-#define FA_LDS __attribute__((address_space(3)))
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// ---------------------------------------------------------------- tile geometry
-template <int D, int BC, int NW, int MODE>
-struct Geo {
-  static constexpr int EB = MODE == MODE_FP8 ? 1 : 2;      // bytes per element in LDS
-  static constexpr int PLANES = MODE == MODE_F32 ? 2 : 1;  // hi/lo planes for the fp32 split
-  static constexpr int ROWB = D * EB;                      // bytes per LDS tile row
-  static constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
-  static constexpr int TILEB = BC * ROWB;                  // one plane of one tensor
-  static constexpr int STAGEB = 2 * PLANES * TILEB;        // K and V planes of one stage
-  static constexpr int LDSB = 2 * STAGEB;                  // double buffered
-  static constexpr int NT = NW * 64;                       // threads
-  static constexpr int UNITS = TILEB / 16;                 // 16-byte LDS chunks per plane
-  static constexpr int UPT = UNITS / NT;                   // chunks per thread per tensor
-  static constexpr int BR = 32 * NW;                       // query rows per workgroup
-  // rows that share one 256-byte span of LDS banks
-  static constexpr int RPP = CPR >= 16 ? 1 : 16 / CPR;
-  static_assert(UNITS % NT == 0, "tile must split evenly over the threads");
-  static_assert(BC % 32 == 0, "B_c is a multiple of 32");
-  static_assert(MODE != MODE_FP8 || BC % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
-  static_assert(LDSB <= 160 * 1024, "LDS budget");
-};
-
-// XOR swizzles of the 16-byte chunk index.  K tiles are read 32 rows at a
-// time at one logical chunk (MFMA A operand); V tiles are read with the
-// transpose loads, a few rows by a few adjacent chunks at a time.
-template <int D, int BC, int NW, int MODE>
-__device__ __forceinline__ int swz_k(int row) {
-  using G = Geo<D, BC, NW, MODE>;
-  constexpr int span = G::CPR < 16 ? G::CPR : 16;
-  return (row / G::RPP) % span;
-}
-template <int D, int BC, int NW, int MODE>
-__device__ __forceinline__ int swz_v(int row) {
-  using G = Geo<D, BC, NW, MODE>;
-  if constexpr (MODE == MODE_FP8) {
-    // transposed byte reads touch rows {r%4, (r/8)%2} x 2 chunks
-    if constexpr (G::CPR >= 16) return 2 * ((row & 3) + 4 * ((row >> 3) & 1));
-    else if constexpr (G::CPR == 8) return 2 * (((row & 3) >> 1) + 2 * ((row >> 3) & 1));
-    else return 2 * ((row >> 3) & 1);
-  } else {
-    // transposed 16-bit reads touch 4 consecutive rows x 4 chunks
-    constexpr int groups = G::CPR >= 16 ? 4 : G::CPR / 4;
-    return 4 * ((row / G::RPP) % groups);
-  }
-}
-
-// ---------------------------------------------------------------- small helpers
-__device__ __forceinline__ float swap_halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
-}
-__device__ __forceinline__ float swap_halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
-
-__device__ __forceinline__ i32x4 lds_read16(const char FA_LDS* p) {
-  return *reinterpret_cast<const i32x4 FA_LDS*>(p);
-}
-__device__ __forceinline__ void lds_write16(char FA_LDS* p, i32x4 v) {
-  *reinterpret_cast<i32x4 FA_LDS*>(p) = v;
-}
-// One 16-byte-per-lane HBM -> LDS load (global_load_lds_dwordx4): lane l's
-// 16 bytes land at LDS byte lds + 16*l.  Issued from asm so that the
-// compiler's wait insertion does not treat it as aliasing every later LDS read
-// (it cannot tell the stages apart); completion is awaited explicitly with
-// s_waitcnt vmcnt(0) before the workgroup barrier that publishes the tile.
-__device__ __forceinline__ void dma16(const void* gsrc, const char FA_LDS* lds) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)lds;
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0v) : "memory");
-}
-__device__ __forceinline__ i16x4 lds_tr16(const char FA_LDS* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<i16x4 FA_LDS*>(const_cast<char FA_LDS*>(p)));
-}
-__device__ __forceinline__ i32x2 lds_tr8(const char FA_LDS* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(reinterpret_cast<i32x2 FA_LDS*>(const_cast<char FA_LDS*>(p)));
-}
-
-__device__ __forceinline__ f32x16 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
-  // format codes 0/0 = e4m3 for both operands; E8M0 scale 127 = 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
-// round-to-nearest-even float -> bf16 bits (the hardware conversion)
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));   // v_cvt_pk_bf16_f32
-}
-__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// split 8 fp32 values into bf16 hi and lo parts (x ~= hi + lo)
-__device__ __forceinline__ void split8(const float* x, i32x4& hi, i32x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t h = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-    float r0 = x[2 * i] - bf16_lo_to_f32(h);
-    float r1 = x[2 * i + 1] - bf16_hi_to_f32(h);
-    hi[i] = (int)h;
-    lo[i] = (int)pack_bf16x2(r0, r1);
-  }
-}
-
-// map a workgroup id to (head, row block); heaviest causal row blocks first
-template <bool CAUSAL>
-__device__ __forceinline__ void map_block(const Params& p, int id, int& bh, int& rb) {
-  if (p.xcd_heads) {
-    const int xcd = id & 7, slot = id >> 3;
-    bh = xcd + 8 * (slot / p.nrb);
-    rb = slot % p.nrb;
-  } else {
-    bh = id % p.BH;
-    rb = id / p.BH;
-  }
-  if (CAUSAL) rb = p.nrb - 1 - rb;
-}
-
 // ---------------------------------------------------------------- the kernel
-template <int D, int BC, int NW, int MODE, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
-  using G = Geo<D, BC, NW, MODE>;
+template <int D, int BC, int NW, int MODE, bool CAUSAL, int STAGES = 2>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_fwd_kernel(Params p) {
+  using G = Geo<D, BC, NW, MODE, STAGES>;
   constexpr int KB = BC / 32;                       // 32-key blocks per tile
   constexpr int NDB = D / 32;                       // 32-wide blocks of the head dim
   constexpr int QK_STEPS = MODE == MODE_FP8 ? D / 64 : D / 16;   // MFMA k-steps over d
@@ -308,8 +155,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       const int off = blk + lane * 16;
       const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
       const int64_t grow = (int64_t)min(row0 + row, N - 1) * G::ROWB;
-      const char* ks = kglob + grow + ((pc ^ swz_k<D, BC, NW, MODE>(row)) << 4);
-      const char* vs = vglob + grow + ((pc ^ swz_v<D, BC, NW, MODE>(row)) << 4);
+      const char* ks = kglob + grow + ((pc ^ swz_k<G::CPR>(row)) << 4);
+      const char* vs = vglob + grow + ((pc ^ swz_v<G::CPR, MODE>(row)) << 4);
       dma16(ks, kdst + blk);
       dma16(vs, vdst + blk);
     }
@@ -335,8 +182,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
     for (int i = 0; i < (DMA ? 0 : G::UPT); ++i) {
       const int u = tid + i * G::NT;
       const int row = u / G::CPR, ch = u % G::CPR;
-      const int koff = row * G::ROWB + ((ch ^ swz_k<D, BC, NW, MODE>(row)) << 4);
-      const int voff = row * G::ROWB + ((ch ^ swz_v<D, BC, NW, MODE>(row)) << 4);
+      const int koff = row * G::ROWB + ((ch ^ swz_k<G::CPR>(row)) << 4);
+      const int voff = row * G::ROWB + ((ch ^ swz_v<G::CPR, MODE>(row)) << 4);
       float kx[8], vx[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -352,8 +199,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       lds_write16(vbase + G::TILEB + voff, vl);
     }
   };
+  constexpr int TILE_LOADS = 2 * G::UPT;               // DMA instructions per thread per tile
   auto wait_loads = [&]() __attribute__((always_inline)) {
-    if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (DMA) wait_vmcnt<0>();
   };
 
   // ---------------- running state
@@ -391,14 +239,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
       for (int kb = 0; kb < KB; ++kb) {
         const int row = 32 * kb + n;
         if constexpr (MODE == MODE_FP8) {
-          const int sw = swz_k<D, BC, NW, MODE>(row);
+          const int sw = swz_k<G::CPR>(row);
           const char FA_LDS* rp = kbase + row * G::ROWB;
           i32x4 a0 = lds_read16(rp + (((4 * c + 2 * hf) ^ sw) << 4));
           i32x4 a1 = lds_read16(rp + (((4 * c + 2 * hf + 1) ^ sw) << 4));
           i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
           st[kb] = mfma_fp8(a, q8[c], st[kb]);
         } else {
-          const int off = row * G::ROWB + (((2 * c + hf) ^ swz_k<D, BC, NW, MODE>(row)) << 4);
+          const int off = row * G::ROWB + (((2 * c + hf) ^ swz_k<G::CPR>(row)) << 4);
           bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kbase + off));
           st[kb] = mfma_bf16(a, qa[c], st[kb]);
           if constexpr (MODE == MODE_F32) {
@@ -433,6 +281,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
     const float m_tile = mraw * c2;
     const bool grow = m_tile > m_run + TAU;
     if (__builtin_amdgcn_ballot_w64(grow)) {
+      asm volatile("" ::: "memory");   // keep this a real (rarely taken) branch, not a select
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
       m_run = grow ? m_tile : m_run;
       l_run *= alpha;
@@ -475,7 +324,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
           for (int t = 0; t < 4; ++t) {
             const int row = 64 * g + 16 * t + v_row_part;
             const int col = 32 * db + v_col_part;        // bytes
-            const int off = row * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row)) << 4) | (col & 15));
+            const int off = row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row)) << 4) | (col & 15));
             i32x2 r = lds_tr8(vbase + off);
             va[2 * t] = r[0];
             va[2 * t + 1] = r[1];
@@ -503,8 +352,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
         for (int db = 0; db < NDB; ++db) {
           const int row = 32 * kb + 16 * cp + v_row_part;
           const int col = 32 * db * 2 + v_col_part;      // bytes
-          const int off0 = row * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row)) << 4) | (col & 15));
-          const int off1 = (row + 8) * G::ROWB + ((((col >> 4) ^ swz_v<D, BC, NW, MODE>(row + 8)) << 4) | (col & 15));
+          const int off0 = row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row)) << 4) | (col & 15));
+          const int off1 = (row + 8) * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row + 8)) << 4) | (col & 15));
           i16x4 lo = lds_tr16(vbase + off0), hi = lds_tr16(vbase + off1);
           bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = mfma_bf16(a, pbh, oacc[db]);
@@ -519,29 +368,53 @@ __global__ __launch_bounds__(NW * 64, 2) void fa_fwd_kernel(Params p) {
     }
   };
 
-  if constexpr (DMA) {
-    issue_tile(0, smem);
-  } else {
-    load_tile(0);
-    store_tile(smem);
-  }
-  wait_loads();
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    char FA_LDS* const cur = smem + (j & 1) * G::STAGEB;
-    char FA_LDS* const next = smem + ((j & 1) ^ 1) * G::STAGEB;
-    const bool more = j + 1 < n_tiles;
-    if (more) {                       // start fetching tile j+1 into the other stage
-      if constexpr (DMA) issue_tile(j + 1, next);
-      else load_tile(j + 1);
-    }
-    if (j < wave_tiles) compute_tile(j, cur);
-    if constexpr (!DMA) {
-      if (more) store_tile(next);
+  if constexpr (STAGES == 2) {
+    if constexpr (DMA) {
+      issue_tile(0, smem);
+    } else {
+      load_tile(0);
+      store_tile(smem);
     }
     wait_loads();
     __syncthreads();
+
+    for (int j = 0; j < n_tiles; ++j) {
+      char FA_LDS* const cur = smem + (j & 1) * G::STAGEB;
+      char FA_LDS* const next = smem + ((j & 1) ^ 1) * G::STAGEB;
+      const bool more = j + 1 < n_tiles;
+      if (more) {                       // start fetching tile j+1 into the other stage
+        if constexpr (DMA) issue_tile(j + 1, next);
+        else load_tile(j + 1);
+      }
+      if (j < wave_tiles) compute_tile(j, cur);
+      if constexpr (!DMA) {
+        if (more) store_tile(next);
+      }
+      wait_loads();
+      __syncthreads();
+    }
+  } else {
+    // three-stage ring: tile j+2 is in flight while tile j is consumed; the
+    // wait at the end of iteration j covers tile j+1 only
+    issue_tile(0, smem);
+    if (n_tiles > 1) {
+      issue_tile(1, smem + G::STAGEB);
+      wait_vmcnt<TILE_LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+    int cur_s = 0;                      // stage of tile j
+    for (int j = 0; j < n_tiles; ++j) {
+      const int ahead_s = cur_s == 0 ? 2 : cur_s - 1;   // (j + 2) % 3
+      const bool ahead = j + 2 < n_tiles;
+      if (ahead) issue_tile(j + 2, smem + ahead_s * G::STAGEB);
+      if (j < wave_tiles) compute_tile(j, smem + cur_s * G::STAGEB);
+      if (ahead) wait_vmcnt<TILE_LOADS>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      cur_s = cur_s == 2 ? 0 : cur_s + 1;
+    }
   }
 
   // ---------------- epilogue: O = O / l, L = ln2 * (m + log2 l)
