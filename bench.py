@@ -78,7 +78,7 @@ def device_inputs(w):
     return x, conv(x.q), conv(x.k), conv(x.v)
 
 
-def time_workload(w, steps, warmup):
+def time_workload(w, steps, warmup, settle_s=0.25):
     import torch
     import exact_io_aware_48_amd as fa
     x, q, k, v = device_inputs(w)
@@ -91,6 +91,13 @@ def time_workload(w, steps, warmup):
                                        causal=w.causal, stream=stream)
     else:
         launch = lambda: fa.fa_fwd(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal, stream=stream)
+    # untimed: let the clocks settle on this very step, then the W warmup steps
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            launch()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         launch()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -123,17 +130,23 @@ def copy_calibration(nbytes=256 * 2**20, reps=3):
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(w):
-    from oracle import attention_naive        # the float64 oracle, as it stands
+def cpu_baseline(w, min_seconds=8.0):
+    """The float64 oracle, as it stands, over the whole workload, repeated until
+    ``min_seconds`` of wall time have passed (bounded: at most 100 passes)."""
+    from oracle import attention_naive
     from workloads import make_inputs
     x = make_inputs(w)
     threads = min(16, len(os.sched_getaffinity(0)))
     q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
-    t0 = time.perf_counter()
-    attention_naive(q, k, v, w.softmax_scale, w.causal, threads=threads)
+    passes, t0 = 0, time.perf_counter()
+    while passes < 100:
+        attention_naive(q, k, v, w.softmax_scale, w.causal, threads=threads)
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
-    return {"value": w.flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole workload ({w.B}x{w.H} heads, N={w.N}, d={w.d}, "
+    return {"value": round(passes * w.flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} passes over the whole workload ({w.B}x{w.H} heads, N={w.N}, d={w.d}, "
                       f"{'causal' if w.causal else 'full'}) in float64 numpy, {dt:.2f} s wall; "
                       f"FLOPs by the same convention as value"}
 
@@ -150,7 +163,7 @@ def _read_counter_csv(d):
     return rows
 
 
-def summarize_pmc(dir_fetch, dir_write, workload_name):
+def summarize_pmc(dir_fetch, dir_write, workload_name, command=""):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, scaled by a copy kernel."""
     from workloads import by_name
     w = by_name(workload_name)
@@ -180,12 +193,38 @@ def summarize_pmc(dir_fetch, dir_write, workload_name):
         "hbm_bytes_per_launch": fetch_b + write_b,
         "compulsory_bytes": w.compulsory_bytes,
         "traffic_over_compulsory": (fetch_b + write_b) / w.compulsory_bytes,
+        "command": command,
     }
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, f"traffic_{workload_name}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+
+
+def summarize_trace(trace_dir, workload_name, command):
+    """Write profiles/kernel_trace_<workload>.txt from a rocprofv3 --kernel-trace --stats run."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
+    rows = []
+    for fn in files:
+        with open(fn) as f:
+            rows += list(csv.DictReader(f))
+    lines = [f"rocprofv3 kernel statistics: {workload_name}",
+             f"command: {command}",
+             f"kernel sources sha: {kernel_source_hash()}",
+             "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}"]
+    for r in rows:
+        name = r["Name"].replace("void ", "")[:60]
+        lines.append(f"{name:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
+                     f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} {float(r['Percentage']):7.2f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"kernel_trace_{workload_name}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 # ------------------------------------------------------------------ main
@@ -205,11 +244,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--settle", type=float, default=0.25, help="seconds of untimed clock-settling steps")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
 
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.command)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -228,7 +273,7 @@ def main():
     w = by_name(args.workload)
     if args.copy_calibration:
         copy_calibration()
-    t = time_workload(w, args.steps, args.warmup)
+    t = time_workload(w, args.steps, args.warmup, args.settle)
     achieved, peak, ai = line_for(w, t, args.steps, args.warmup)
     value = w.flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
     traffic = traffic_for(w.name)
@@ -267,7 +312,7 @@ def main():
         for ow in WORKLOADS:
             if ow.name == w.name:
                 continue
-            ot = time_workload(ow, max(10, args.steps // 4), max(3, args.warmup // 2))
+            ot = time_workload(ow, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle)
             oa, opk, oai = line_for(ow, ot, 0, 0)
             others[ow.name] = {"tflops_kernel": round(oa, 1), "pct_of_dense_peak": round(100 * oa / opk, 2),
                                "kernel_ms_median": round(ot["kernel_ms_median"], 4), "dtype": ow.dtype,
