@@ -39,7 +39,8 @@ HEADLINE = "gpt2s_causal_bf16_b8h12n1024d64"
 METRIC = "attention fwd TFLOP/s and % of MI355X dense MFMA peak at N=1K–16K, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 2516.6, "fp8": 5033.2}   # dense MFMA peaks of the type the products use
 HBM_GBPS = 8000.0
-KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp",
+KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_tile.hpp",
+                  "exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp",
                   "exact_io_aware_48_amd/csrc/fa_api.hip"]
 PROFILES = os.path.join(ROOT, "profiles")
 

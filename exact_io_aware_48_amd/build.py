@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libfa_fwd.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "fa_api.hip")]
-HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_fwd_kernel.hpp")] + [os.path.join(INCLUDE, "fa_fwd.h")]
+HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp")] + [os.path.join(INCLUDE, "fa_fwd.h")]
 
 
 def hipcc():

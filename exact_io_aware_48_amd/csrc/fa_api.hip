@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <climits>
+#include <atomic>
 
 #include "fa_fwd.h"
 #include "fa_fwd_kernel.hpp"
@@ -23,26 +24,27 @@ struct Tile {
   int br() const { return 32 * nw; }
 };
 
-// Shapes per (mode, d), chosen by measurement on MI355X.  Eight waves per
+// Shape per (mode, d), chosen by measurement on MI355X.  Eight waves per
 // workgroup (256 query rows) halve the K/V traffic per FLOP for the large
 // heads; d = 64 keeps four waves so that the short causal rows spread over
 // more workgroups.  d = 256 with 16-bit tiles uses 32-key tiles to stay
-// within 256 VGPRs at two waves per SIMD.
+// within 256 VGPRs at two waves per SIMD.  PP: ping-pong wave groups (the
+// upper half of the waves runs P V one tile late), which pays off for fp8.
 template <int MODE, int D> struct Cfg;
-template <> struct Cfg<fa::MODE_BF16, 64> { static constexpr int BC = 64, NW = 4, ST = 2; };
-template <> struct Cfg<fa::MODE_BF16, 128> { static constexpr int BC = 128, NW = 8, ST = 2; };
-template <> struct Cfg<fa::MODE_BF16, 256> { static constexpr int BC = 32, NW = 8, ST = 2; };
-template <> struct Cfg<fa::MODE_FP8, 64> { static constexpr int BC = 64, NW = 4, ST = 2; };
-template <> struct Cfg<fa::MODE_FP8, 128> { static constexpr int BC = 64, NW = 8, ST = 2; };
-template <> struct Cfg<fa::MODE_FP8, 256> { static constexpr int BC = 64, NW = 8, ST = 2; };
-template <> struct Cfg<fa::MODE_F32, 64> { static constexpr int BC = 64, NW = 4, ST = 2; };
-template <> struct Cfg<fa::MODE_F32, 128> { static constexpr int BC = 64, NW = 4, ST = 2; };
-template <> struct Cfg<fa::MODE_F32, 256> { static constexpr int BC = 32, NW = 4, ST = 2; };
+template <> struct Cfg<fa::MODE_BF16, 64> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
+template <> struct Cfg<fa::MODE_BF16, 128> { static constexpr int BC = 128, NW = 8; static constexpr bool PP = false; };
+template <> struct Cfg<fa::MODE_BF16, 256> { static constexpr int BC = 32, NW = 8; static constexpr bool PP = false; };
+template <> struct Cfg<fa::MODE_FP8, 64> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
+template <> struct Cfg<fa::MODE_FP8, 128> { static constexpr int BC = 64, NW = 8; static constexpr bool PP = true; };
+template <> struct Cfg<fa::MODE_FP8, 256> { static constexpr int BC = 64, NW = 8; static constexpr bool PP = true; };
+template <> struct Cfg<fa::MODE_F32, 64> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
+template <> struct Cfg<fa::MODE_F32, 128> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
+template <> struct Cfg<fa::MODE_F32, 256> { static constexpr int BC = 32, NW = 4; static constexpr bool PP = false; };
 
 template <int MODE, int D>
 Tile tile_for() {
-  constexpr int BC = Cfg<MODE, D>::BC, NW = Cfg<MODE, D>::NW, ST = Cfg<MODE, D>::ST;
-  return Tile{BC, NW, fa::Geo<D, BC, NW, MODE, ST>::LDSB};
+  using C = Cfg<MODE, D>;
+  return Tile{C::BC, C::NW, fa::Geo<D, C::BC, C::NW, MODE, C::PP>::LDSB};
 }
 
 Tile lookup_tile(int mode, int d) {
@@ -59,13 +61,48 @@ Tile lookup_tile(int mode, int d) {
   }
 }
 
+// How many workgroups of `kern` the current device keeps resident at once,
+// and its CUs per XCD (0 when the CU count is not a multiple of the 8 XCDs).
+// Queried once per kernel and device and cached: the values never change.
+constexpr int kMaxDevices = 64;
+struct Residency {
+  int resident;
+  int cus_per_xcd;
+};
+Residency residency(const void* kern, int threads, std::atomic<int>* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return {0, 0};
+  }
+  int packed = cache[dev].load(std::memory_order_relaxed);
+  if (packed == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return {0, 0};
+    }
+    packed = (cus * per_cu) * 1024 + (cus % 8 == 0 ? cus / 8 : 0) + 1;   // + 1: never 0 once known
+    cache[dev].store(packed, std::memory_order_relaxed);
+  }
+  return {(packed - 1) / 1024, (packed - 1) % 1024};
+}
+
 template <int MODE, int D, bool CAUSAL>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
-  constexpr int BC = Cfg<MODE, D>::BC, NW = Cfg<MODE, D>::NW, ST = Cfg<MODE, D>::ST;
+  using C = Cfg<MODE, D>;
+  constexpr int BC = C::BC, NW = C::NW;
+  void (*kern)(Params) = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP>;
   Params args = p;
+  if constexpr (CAUSAL) {
+    static std::atomic<int> cache[kMaxDevices];   // one per kernel
+    const Residency r = residency(reinterpret_cast<const void*>(kern), NW * 64, cache);
+    args.cus_per_xcd = r.cus_per_xcd;
+    args.zigzag = r.cus_per_xcd > 0 && grid <= r.resident ? 1 : 0;
+  }
   void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, ST>),
-                         dim3(grid), dim3(NW * 64), kargs, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(NW * 64), kargs, 0, stream);
 }
 
 template <int MODE>

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 enum { MODE_BF16 = 0, MODE_FP8 = 1, MODE_F32 = 2 };
@@ -19,6 +21,8 @@ struct Params {
   int N;           // sequence length (queries = keys)
   int nrb;         // row blocks per head = ceil(N / B_r)
   int xcd_heads;   // 1: heads are spread over XCDs head-major (BH % 8 == 0)
+  int cus_per_xcd; // compute units per XCD (0: unknown)
+  int zigzag;      // causal grid fully resident: deal row blocks to CUs zig-zag (see map_block)
   float c2;        // |scale| * descale_q * descale_k * log2(e)
   float out_mul;   // factor applied to O before dividing by l (fp8: descale_v / 256)
   uint32_t qsign;  // XOR mask on Q's sign bits (negative scale)
@@ -40,26 +44,30 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------- tile geometry
-template <int D, int BC, int NW, int MODE, int STAGES = 2>
+template <int D, int BC, int NW, int MODE, bool PP = false>
 struct Geo {
   static constexpr int EB = MODE == MODE_FP8 ? 1 : 2;      // bytes per element in LDS
   static constexpr int PLANES = MODE == MODE_F32 ? 2 : 1;  // hi/lo planes for the fp32 split
   static constexpr int ROWB = D * EB;                      // bytes per LDS tile row
   static constexpr int CPR = ROWB / 16;                    // 16-byte chunks per row
   static constexpr int TILEB = BC * ROWB;                  // one plane of one tensor
-  static constexpr int STAGEB = 2 * PLANES * TILEB;        // K and V planes of one stage
-  static constexpr int LDSB = STAGES * STAGEB;             // ring of STAGES tiles
+  static constexpr int SLOTB = PLANES * TILEB;             // one ring slot (all planes of one tile)
+  static constexpr int KST = 2;                            // K ring: tile j in use, tile j+1 in flight
+  static constexpr int VST = PP ? 3 : 2;                   // V ring: the ping-pong group also keeps tile j-1
+  static constexpr int LDSB = (KST + VST) * SLOTB;
   static constexpr int NT = NW * 64;                       // threads
   static constexpr int UNITS = TILEB / 16;                 // 16-byte LDS chunks per plane
-  static constexpr int UPT = UNITS / NT;                   // chunks per thread per tensor
+  // a tile smaller than one chunk per thread is staged by its first LOADERS waves
+  static constexpr int UPT = UNITS >= NT ? UNITS / NT : 1; // chunks per loading thread per tensor
+  static constexpr int LOADERS = UNITS >= NT ? NW : UNITS / 64;
   static constexpr int BR = 32 * NW;                       // query rows per workgroup
   // rows that share one 256-byte span of LDS banks
   static constexpr int RPP = CPR >= 16 ? 1 : 16 / CPR;
-  static_assert(UNITS % NT == 0, "tile must split evenly over the threads");
+  static_assert(UNITS >= NT ? UNITS % NT == 0 : UNITS % 64 == 0, "tile must split evenly over the loading waves");
   static_assert(BC % 32 == 0, "B_c is a multiple of 32");
   static_assert(MODE != MODE_FP8 || BC % 64 == 0, "fp8 P.V consumes 64 keys per MFMA");
   static_assert(LDSB <= 160 * 1024, "LDS budget");
-  static_assert(STAGES == 2 || (STAGES == 3 && MODE != MODE_F32), "fp32 staging is double buffered");
+  static_assert(!PP || (MODE != MODE_F32 && NW % 2 == 0), "ping-pong needs DMA staging and an even wave count");
 };
 
 // XOR swizzles of the 16-byte chunk index.  K tiles are read 32 rows at a
@@ -112,6 +120,12 @@ __device__ __forceinline__ void dma16(const void* gsrc, const char FA_LDS* lds) 
   const uint32_t m0v = (uint32_t)(uintptr_t)lds;
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0v) : "memory");
 }
+// The same load addressed as a wave-uniform 64-bit base (SGPRs) plus a
+// per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(const char* sbase, int voff, const char FA_LDS* lds) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)lds;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+}
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (they complete in issue order, so the older ones are then done).
 template <int N>
@@ -154,18 +168,47 @@ __device__ __forceinline__ void split8(const float* x, i32x4& hi, i32x4& lo) {
   }
 }
 
-// map a workgroup id to (head, row block); heaviest causal row blocks first
+// Map a workgroup id to (head, row block).
+// The hardware deals workgroup ids to the 8 XCDs round-robin (XCD = id % 8)
+// and, within an XCD, slots s = id / 8 to its CUs round-robin (CU s % C for
+// C CUs per XCD), so slots s, s + C, s + 2C ... share a CU.
+//   * xcd_heads: all row blocks of a head stay on one XCD (its K/V stream
+//     stays in that XCD's L2).
+//   * causal: row blocks differ in work (row block i has i+1 key tiles of
+//     B_r), so the XCD's work list is ordered heaviest first.  When the whole
+//     grid is resident at once (zigzag), consecutive rounds of C slots take
+//     that list forward, backward, forward ... so every CU's workgroups add up
+//     to about the same number of tiles; otherwise heaviest-first order lets
+//     CUs that free up early take the next-heaviest block.
+__device__ __forceinline__ int zigzag_slot(int s, int total, int C) {
+  const int r = s / C, pos = s - r * C, base = r * C;
+  const int R = min(C, total - base);          // slots in this round
+  return base + ((r & 1) ? R - 1 - pos : pos);
+}
 template <bool CAUSAL>
 __device__ __forceinline__ void map_block(const Params& p, int id, int& bh, int& rb) {
-  if (p.xcd_heads) {
-    const int xcd = id & 7, slot = id >> 3;
-    bh = xcd + 8 * (slot / p.nrb);
-    rb = slot % p.nrb;
+  const int nrb = p.nrb;
+  if constexpr (!CAUSAL) {
+    if (p.xcd_heads) {
+      const int xcd = id & 7, s = id >> 3;
+      bh = xcd + 8 * (s / nrb);
+      rb = s % nrb;
+    } else {
+      bh = id % p.BH;
+      rb = id / p.BH;
+    }
   } else {
-    bh = id % p.BH;
-    rb = id / p.BH;
+    if (p.xcd_heads) {
+      const int xcd = id & 7, s = id >> 3, hpx = p.BH >> 3;
+      const int k = p.zigzag ? zigzag_slot(s, hpx * nrb, p.cus_per_xcd) : s;
+      bh = xcd + 8 * (k % hpx);
+      rb = nrb - 1 - k / hpx;
+    } else {
+      const int k = p.zigzag ? zigzag_slot(id, p.BH * nrb, 8 * p.cus_per_xcd) : id;
+      bh = k % p.BH;
+      rb = nrb - 1 - k / p.BH;
+    }
   }
-  if (CAUSAL) rb = p.nrb - 1 - rb;
 }
 
 }  // namespace fa

@@ -1,0 +1,378 @@
+// Per-wave building blocks shared by the attention kernels: the wave's Q
+// fragment, S^T = K_j Q^T over one LDS tile, masking, the online-softmax
+// exponentials with P packed as an MFMA operand, O^T += V_j^T P^T, the output
+// epilogue, and the HBM -> LDS staging of a K or V tile.
+//
+// Register layouts (v_mfma_f32_32x32x16_bf16 on a wave64; lane = 32*hf + n):
+//   S^T accumulator (32 keys x 32 queries): lane holds query n, element i is
+//     key 8*(i/4) + 4*hf + i%4 of the 32-key block.
+//   O^T accumulator (32 dims x 32 queries): lane holds query n, element i is
+//     dim 8*(i/4) + 4*hf + i%4 of the 32-dim block.
+// Because the sum over the MFMA's k dimension does not care about the order
+// of k, P^T is fed from the S^T registers as they are, and the V^T operand is
+// read in the same key order with the LDS transpose loads.
+#pragma once
+
+#include <type_traits>
+
+#include "fa_common.hpp"
+
+namespace fa {
+
+template <int D, int BC, int NW, int MODE>
+struct Tile {
+  using G = Geo<D, BC, NW, MODE>;
+  static constexpr int KB = BC / 32;                                // 32-key blocks per tile
+  static constexpr int NDB = D / 32;                                // 32-wide blocks of the head dim
+  static constexpr int QK_STEPS = MODE == MODE_FP8 ? D / 64 : D / 16;   // MFMA k-steps over d
+  static constexpr int PV_STEPS = MODE == MODE_FP8 ? BC / 64 : BC / 16; // MFMA k-steps over keys
+  // lazy-rescale threshold (log2 units); fp8 keeps P <= 1 so that 256 * P fits e4m3
+  static constexpr float TAU = MODE == MODE_FP8 ? 0.f : 8.f;
+
+  // the wave's 32 queries as the B operand of S^T = K Q^T
+  struct QFrag {
+    bf16x8 a[MODE == MODE_FP8 ? 1 : QK_STEPS];   // bf16 values (fp32 mode: hi parts)
+    bf16x8 l[MODE == MODE_F32 ? QK_STEPS : 1];   // fp32 mode: lo parts
+    i32x8 f8[MODE == MODE_FP8 ? QK_STEPS : 1];   // fp8 bytes
+  };
+  // P of one tile as the B operand of O^T += V^T P^T
+  //   bf16/fp32: element i of step s <- key 16*s + 8*(i/4) + 4*hf + i%4 (hi parts; lo in l)
+  //   fp8:       byte 16*kb' + i of step g <- key 64*g + 32*kb' + 8*(i/4) + 4*hf + i%4, x256
+  struct PFrag {
+    i32x4 h[MODE == MODE_FP8 ? 1 : PV_STEPS];    // bf16 pairs
+    i32x4 l[MODE == MODE_F32 ? PV_STEPS : 1];
+    i32x8 f8[MODE == MODE_FP8 ? PV_STEPS : 1];
+  };
+  struct Lane {
+    int n, hf;                  // query column, lane half
+    int v_row, v_col;           // per-lane parts of the V^T transpose-read address
+  };
+
+  static __device__ __forceinline__ Lane lane_info(int lane) {
+    Lane ln;
+    ln.n = lane & 31;
+    ln.hf = lane >> 5;
+    const int grp = lane >> 4;  // 16-lane group
+    if constexpr (MODE == MODE_FP8) {
+      const int isrc = (lane & 15) >> 1;  // which of the 8 returned bytes this lane sources
+      ln.v_row = 8 * (isrc >> 2) + 4 * ln.hf + (isrc & 3);
+      ln.v_col = 16 * (grp & 1) + 8 * (lane & 1);
+    } else {
+      ln.v_row = 4 * ln.hf + ((lane >> 2) & 3);
+      ln.v_col = 2 * (16 * (grp & 1) + 4 * (lane & 3));
+    }
+    return ln;
+  }
+
+  // Q slice of query my_q (zeros past the end) -> registers; qsign flips the
+  // sign bits when the softmax scale is negative.
+  static __device__ __forceinline__ void load_q(const Params& p, int64_t head_off, int my_q, const Lane& ln, QFrag& q) {
+    const bool valid = my_q < p.N;
+    const int sgn = (int)p.qsign;
+    if constexpr (MODE == MODE_BF16) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + head_off + (int64_t)my_q * D);
+#pragma unroll
+      for (int c = 0; c < QK_STEPS; ++c) {
+        i32x4 w = valid ? src[2 * c + ln.hf] : i32x4{0, 0, 0, 0};
+        w ^= i32x4{sgn, sgn, sgn, sgn};
+        q.a[c] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else if constexpr (MODE == MODE_FP8) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint8_t*>(p.q) + head_off + (int64_t)my_q * D);
+#pragma unroll
+      for (int c = 0; c < QK_STEPS; ++c) {
+        i32x4 w0 = valid ? src[4 * c + 2 * ln.hf] : i32x4{0, 0, 0, 0};
+        i32x4 w1 = valid ? src[4 * c + 2 * ln.hf + 1] : i32x4{0, 0, 0, 0};
+        w0 ^= i32x4{sgn, sgn, sgn, sgn};
+        w1 ^= i32x4{sgn, sgn, sgn, sgn};
+        q.f8[c] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      }
+    } else {
+      const float* src = static_cast<const float*>(p.q) + head_off + (int64_t)my_q * D;
+#pragma unroll
+      for (int c = 0; c < QK_STEPS; ++c) {
+        float x[8];
+        if (valid) {
+          f32x4 a = *reinterpret_cast<const f32x4*>(src + 16 * c + 8 * ln.hf);
+          f32x4 b = *reinterpret_cast<const f32x4*>(src + 16 * c + 8 * ln.hf + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = 0.f;
+        }
+        if (p.qsign) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = -x[i];
+        }
+        i32x4 hi, lo;
+        split8(x, hi, lo);
+        q.a[c] = __builtin_bit_cast(bf16x8, hi);
+        q.l[c] = __builtin_bit_cast(bf16x8, lo);
+      }
+    }
+  }
+
+  // ---- single MFMA items.  A QK item (c, kb) adds d-step c of key block kb
+  // to S^T; a PV item (s, db) adds key-step s to d-block db of O^T.  Each
+  // item's A operand is one LDS read (fp8: two, or four transposed reads).
+  using Op = typename std::conditional<MODE == MODE_FP8, i32x8, bf16x8>::type;
+
+  static __device__ __forceinline__ Op k_operand(const char FA_LDS* kbase, int c, int kb, const Lane& ln) {
+    const int row = 32 * kb + ln.n;
+    if constexpr (MODE == MODE_FP8) {
+      const int sw = swz_k<G::CPR>(row);
+      const char FA_LDS* rp = kbase + row * G::ROWB;
+      i32x4 a0 = lds_read16(rp + (((4 * c + 2 * ln.hf) ^ sw) << 4));
+      i32x4 a1 = lds_read16(rp + (((4 * c + 2 * ln.hf + 1) ^ sw) << 4));
+      return i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    } else {
+      return __builtin_bit_cast(bf16x8, lds_read16(kbase + row * G::ROWB + (((2 * c + ln.hf) ^ swz_k<G::CPR>(row)) << 4)));
+    }
+  }
+  static __device__ __forceinline__ void qk_mma(f32x16 (&st)[KB], int c, int kb, const Op& a, const QFrag& q) {
+    if constexpr (MODE == MODE_FP8) st[kb] = mfma_fp8(a, q.f8[c], st[kb]);
+    else st[kb] = mfma_bf16(a, q.a[c], st[kb]);
+  }
+  static __device__ __forceinline__ Op v_operand(const char FA_LDS* vbase, int s, int db, const Lane& ln) {
+    if constexpr (MODE == MODE_FP8) {               // 64 keys per step
+      int va[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = 64 * s + 16 * t + ln.v_row;
+        const int col = 32 * db + ln.v_col;          // bytes
+        const int off = row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row)) << 4) | (col & 15));
+        i32x2 r = lds_tr8(vbase + off);
+        va[2 * t] = r[0];
+        va[2 * t + 1] = r[1];
+      }
+      return i32x8{va[0], va[1], va[2], va[3], va[4], va[5], va[6], va[7]};
+    } else {                                        // 16 keys per step
+      const int row = 16 * s + ln.v_row;
+      const int col = 32 * db * 2 + ln.v_col;        // bytes
+      const int off0 = row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row)) << 4) | (col & 15));
+      const int off1 = (row + 8) * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row + 8)) << 4) | (col & 15));
+      i16x4 lo = lds_tr16(vbase + off0), hi = lds_tr16(vbase + off1);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  }
+  static __device__ __forceinline__ void pv_mma(f32x16 (&oacc)[NDB], int s, int db, const Op& a, const PFrag& pf) {
+    if constexpr (MODE == MODE_FP8) oacc[db] = mfma_fp8(a, pf.f8[s], oacc[db]);
+    else oacc[db] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pf.h[s]), oacc[db]);
+  }
+
+  // st = K Q^T for the tile at kbase (rows: keys, columns: this wave's queries)
+  static __device__ __forceinline__ void qk(f32x16 (&st)[KB], const char FA_LDS* kbase, const QFrag& q, const Lane& ln) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < QK_STEPS; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if constexpr (MODE == MODE_F32) {
+          const int row = 32 * kb + ln.n;
+          const int off = row * G::ROWB + (((2 * c + ln.hf) ^ swz_k<G::CPR>(row)) << 4);
+          bf16x8 a = __builtin_bit_cast(bf16x8, lds_read16(kbase + off));
+          bf16x8 al = __builtin_bit_cast(bf16x8, lds_read16(kbase + G::TILEB + off));
+          st[kb] = mfma_bf16(a, q.a[c], st[kb]);
+          st[kb] = mfma_bf16(a, q.l[c], st[kb]);
+          st[kb] = mfma_bf16(al, q.a[c], st[kb]);
+        } else {
+          qk_mma(st, c, kb, k_operand(kbase, c, kb, ln), q);
+        }
+      }
+    }
+  }
+
+  // scores of keys past lim (relative to the tile start and to 4*hf) -> -inf.
+  // Callers branch around it: only diagonal and ragged tiles need it, and
+  // the compiler would otherwise speculate it into every tile.
+  static __device__ __forceinline__ void mask(f32x16 (&st)[KB], int lim) {
+    asm volatile("" ::: "memory");   // keeps the caller's branch a real branch
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        st[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3)) > lim ? -INFINITY : st[kb][i];
+  }
+
+  // ---- the online-softmax step of one score tile, as a sequence of slices
+  // (a caller may run other work between them).  In order:
+  //   NMAX slices   partial maxima over 8 scores each
+  //   1 slice       the row max (both lane halves), the new running max,
+  //                 alpha = 2^(m_old - m_new) and the exponent base in use
+  //   NEXP slices   P = 2^(c2 * s - m) for 4 scores each (masked scores are
+  //                 -inf and c2 > 0, so their P is exactly 0)
+  //   NPACK slices  4 probabilities packed into the P operand and added, in
+  //                 fp32 and before rounding, to this lane half's row sum
+  // Rescaling: only when some row's maximum grew by more than TAU (log2
+  // units) over the base in use, which keeps exponents <= 2^TAU; O and l
+  // always share one base, so the result is the same.
+  static constexpr int NMAX = 2 * KB, NEXP = 4 * KB, NPACK = 4 * KB;
+  static constexpr int NSLICES = NMAX + 1 + NEXP + NPACK;
+  struct Softmax {
+    float mpart[NMAX];
+    float alpha;     // factor for O and l (1 when the base is kept)
+    bool grow;       // this lane's base changed
+    float m_use;     // exponent base (0 while nothing is seen yet)
+    float psum[2];
+  };
+
+  template <int SL>
+  static __device__ __forceinline__ void softmax_slice(f32x16 (&st)[KB], Softmax& sm, float& m_run, float c2, PFrag& pf) {
+    if constexpr (SL < NMAX) {
+      const int kb = SL / 2, i0 = 8 * (SL % 2);
+      // v_maximum3_f32: no NaN canonicalisation of the inputs, -inf handled as usual
+      float m = st[kb][i0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m = __builtin_elementwise_maximum(m, st[kb][i0 + i]);
+      sm.mpart[SL] = m;
+    } else if constexpr (SL == NMAX) {
+      float m = sm.mpart[0];
+#pragma unroll
+      for (int i = 1; i < NMAX; ++i) m = __builtin_elementwise_maximum(m, sm.mpart[i]);
+      const float m_tile = swap_halves_max(m) * c2;
+      sm.grow = m_tile > m_run + TAU;
+      sm.alpha = sm.grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
+      m_run = sm.grow ? m_tile : m_run;
+      sm.m_use = m_run == -INFINITY ? 0.f : m_run;
+    } else if constexpr (SL < NMAX + 1 + NEXP) {
+      constexpr int g = SL - NMAX - 1;
+      const int kb = g / 4, i0 = 4 * (g % 4);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = st[kb][i0 + i];
+        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], c2, -sm.m_use));
+        st[kb][i0 + i] = x[i];
+      }
+    } else {
+      constexpr int g = SL - NMAX - 1 - NEXP;
+      const int kb = g / 4, i0 = 4 * (g % 4);
+      float x0 = st[kb][i0], x1 = st[kb][i0 + 1], x2 = st[kb][i0 + 2], x3 = st[kb][i0 + 3];
+      if constexpr (MODE == MODE_FP8) {
+        // step g/8, word g%8 <- scores 4g .. 4g+3 of the tile
+        int word = 0;
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x0 * 256.f, x1 * 256.f, word, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x2 * 256.f, x3 * 256.f, word, true);
+        pf.f8[g / 8][g % 8] = word;
+      } else {
+        // step g/2, words 2*(g%2) and 2*(g%2)+1 <- scores 4g .. 4g+3 of the tile
+        int h0 = (int)pack_bf16x2(x0, x1), h1 = (int)pack_bf16x2(x2, x3);
+        pf.h[g / 2][2 * (g % 2)] = h0;
+        pf.h[g / 2][2 * (g % 2) + 1] = h1;
+        if constexpr (MODE == MODE_F32) {
+          int l0 = (int)pack_bf16x2(x0 - bf16_lo_to_f32(h0), x1 - bf16_hi_to_f32(h0));
+          int l1 = (int)pack_bf16x2(x2 - bf16_lo_to_f32(h1), x3 - bf16_hi_to_f32(h1));
+          pf.l[g / 2][2 * (g % 2)] = l0;
+          pf.l[g / 2][2 * (g % 2) + 1] = l1;
+        }
+      }
+      const float part = (x0 + x1) + (x2 + x3);
+      sm.psum[g & 1] = g < 2 ? part : sm.psum[g & 1] + part;
+    }
+  }
+  template <int A, int B>
+  static __device__ __forceinline__ void softmax_slices(f32x16 (&st)[KB], Softmax& sm, float& m_run, float c2, PFrag& pf) {
+    if constexpr (A < B) {
+      softmax_slice<A>(st, sm, m_run, c2, pf);
+      softmax_slices<A + 1, B>(st, sm, m_run, c2, pf);
+    }
+  }
+
+  // oacc += V^T P^T for the tile at vbase
+  static __device__ __forceinline__ void pv(f32x16 (&oacc)[NDB], const char FA_LDS* vbase, const PFrag& pf, const Lane& ln) {
+#pragma unroll
+    for (int s = 0; s < PV_STEPS; ++s) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        if constexpr (MODE == MODE_F32) {
+          const int row = 16 * s + ln.v_row;
+          const int col = 32 * db * 2 + ln.v_col;      // bytes
+          const int off0 = row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row)) << 4) | (col & 15));
+          const int off1 = (row + 8) * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row + 8)) << 4) | (col & 15));
+          i16x4 lo = lds_tr16(vbase + off0), hi = lds_tr16(vbase + off1);
+          i16x4 lo2 = lds_tr16(vbase + G::TILEB + off0), hi2 = lds_tr16(vbase + G::TILEB + off1);
+          bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          bf16x8 al = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8 ph = __builtin_bit_cast(bf16x8, pf.h[s]), pl = __builtin_bit_cast(bf16x8, pf.l[s]);
+          oacc[db] = mfma_bf16(a, ph, oacc[db]);
+          oacc[db] = mfma_bf16(a, pl, oacc[db]);
+          oacc[db] = mfma_bf16(al, ph, oacc[db]);
+        } else {
+          pv_mma(oacc, s, db, v_operand(vbase, s, db, ln), pf);
+        }
+      }
+    }
+  }
+
+  // O = out_mul * O / l and L = ln2 * (m + log2 l) for query my_q
+  static __device__ __forceinline__ void store(const Params& p, int64_t head_off, int bh, int my_q, const Lane& ln,
+                                               const f32x16 (&oacc)[NDB], float m_run, float l_run) {
+    const float l_tot = swap_halves_sum(l_run);
+    const float inv = p.out_mul / l_tot;
+    if (my_q >= p.N) return;
+    if (ln.hf == 0) p.lse[(int64_t)bh * p.N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * ln.hf;
+        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
+        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        if constexpr (MODE == MODE_F32) {
+          float* dst = static_cast<float*>(p.o) + head_off + (int64_t)my_q * D + col;
+          *reinterpret_cast<f32x4*>(dst) = f32x4{x0, x1, x2, x3};
+        } else {
+          uint16_t* dst = static_cast<uint16_t*>(p.o) + head_off + (int64_t)my_q * D + col;
+          *reinterpret_cast<i32x2*>(dst) = i32x2{(int)pack_bf16x2(x0, x1), (int)pack_bf16x2(x2, x3)};
+        }
+      }
+  }
+};
+
+// HBM -> LDS staging of one K or V tile with global_load_lds_dwordx4 (bf16 and
+// fp8 tiles).  One wave instruction fills 1 KiB of LDS, lane l at byte 16*l;
+// the XOR swizzle is applied by choosing which global chunk each lane
+// fetches.  The per-lane byte offsets inside a full tile do not depend on the
+// tile, so they are computed once; the tile's base address is wave-uniform
+// and travels in SGPRs.  Rows past the end of the sequence re-read row N-1:
+// their scores are masked, so they only ever meet P = 0.
+template <int D, int BC, int NW, int MODE, bool IS_V>
+struct Stager {
+  using G = Geo<D, BC, NW, MODE>;
+  int ofs[G::UPT];
+
+  static __device__ __forceinline__ int swz(int row) {
+    if constexpr (IS_V) return swz_v<G::CPR, MODE>(row);
+    else return swz_k<G::CPR>(row);
+  }
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < G::UPT; ++i) {
+      const int off = (i * NW + wave) * 1024 + lane * 16;
+      const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
+      ofs[i] = row * G::ROWB + ((pc ^ swz(row)) << 4);
+    }
+  }
+  // tile j of the head at glob -> LDS at dst
+  __device__ __forceinline__ void issue(const char* glob, int j, int N, char FA_LDS* dst, int wave, int lane) const {
+    if (G::LOADERS < NW && wave >= G::LOADERS) return;
+    const int row0 = j * BC;
+    const char* base = glob + (int64_t)row0 * G::ROWB;
+    if (row0 + BC <= N) {
+#pragma unroll
+      for (int i = 0; i < G::UPT; ++i) dma16_s(base, ofs[i], dst + (i * NW + wave) * 1024);
+    } else {
+      const int last = N - 1 - row0;
+#pragma unroll
+      for (int i = 0; i < G::UPT; ++i) {
+        const int off = (i * NW + wave) * 1024 + lane * 16;
+        const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
+        dma16_s(base, min(row, last) * G::ROWB + ((pc ^ swz(row)) << 4), dst + (i * NW + wave) * 1024);
+      }
+    }
+  }
+};
+
+}  // namespace fa
