@@ -7,11 +7,14 @@ softmax, masking, normalisation, O and logsumexp stores) runs in that one
 kernel launch.  Inputs are seeded synthetic tensors (``workloads``) made
 resident in HBM before the timed region.
 
+The K timed steps are K launches of the entry point, bracketed by device
+synchronisation (``--graph``: captured once into a HIP graph and replayed).
+
 Prints one JSON line.  ``value`` is whole-job throughput in TFLOP/s by the
 convention 4*B*H*N^2*d (halved for the causal mask) over the K timed steps on
 the host clock.  ``roofline.achieved`` is the same FLOP count per launch over
-the kernel's mean duration from HIP events recorded around every launch on
-the launch stream.  ``traffic`` is the HBM bytes per launch measured with
+the kernel's mean duration from HIP events on the launch stream around every
+launch (around the replay with ``--graph``, divided by K).  ``traffic`` is the HBM bytes per launch measured with
 rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same
 counters give for a plain copy of known size), read from profiles/ and only
 when the kernel sources are unchanged since that measurement.
@@ -79,19 +82,27 @@ def device_inputs(w):
     return x, conv(x.q), conv(x.k), conv(x.v)
 
 
-def time_workload(w, steps, warmup, settle_s=0.25):
+def time_workload(w, steps, warmup, settle_s=0.25, graph=False):
+    """Time exactly `steps` launches of the forward on workload w.
+
+    graph=False (default): eager launches, one event pair around each launch;
+    the per-launch time is the mean over the pairs.
+    graph=True: the `steps` launches are captured once into a HIP graph and the
+    timed region is one replay of it (the kernels run back to back, with no
+    host launch path in between); the per-launch time is the replay's event
+    time / steps, which includes the gap between dependent kernels.
+    """
     import torch
     import exact_io_aware_48_amd as fa
     x, q, k, v = device_inputs(w)
     out_dtype = torch.float32 if w.dtype == "f32" else torch.bfloat16
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=out_dtype, device="cuda")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
+    # stream=None: the current stream at call time (the capture stream while capturing)
     if w.dtype == "fp8":
-        launch = lambda: fa.fa_fwd_fp8(q, k, v, *x.descale, o=o, lse=lse, scale=w.softmax_scale,
-                                       causal=w.causal, stream=stream)
+        launch = lambda: fa.fa_fwd_fp8(q, k, v, *x.descale, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
     else:
-        launch = lambda: fa.fa_fwd(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal, stream=stream)
+        launch = lambda: fa.fa_fwd(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
     # untimed: let the clocks settle on this very step, then the W warmup steps
     torch.cuda.synchronize()
     t_end = time.perf_counter() + settle_s
@@ -101,6 +112,26 @@ def time_workload(w, steps, warmup, settle_s=0.25):
         torch.cuda.synchronize()
     for _ in range(warmup):
         launch()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                launch()
+        g.replay()                      # untimed: the first replay uploads the graph
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        per = a.elapsed_time(b) / steps
+        return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_mean": per, "kernel_ms_median": per,
+                "kernel_ms_p10": None, "kernel_ms_p90": None, "timing": f"one HIP graph replay of {steps} launches"}
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -117,6 +148,7 @@ def time_workload(w, steps, warmup, settle_s=0.25):
         "kernel_ms_median": kms[len(kms) // 2],
         "kernel_ms_p10": kms[len(kms) // 10],
         "kernel_ms_p90": kms[(9 * len(kms)) // 10],
+        "timing": "eager launches, one event pair per launch",
     }
 
 
@@ -246,6 +278,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--settle", type=float, default=0.25, help="seconds of untimed clock-settling steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one HIP graph replay of the K launches instead of eager launches")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
@@ -274,7 +308,7 @@ def main():
     w = by_name(args.workload)
     if args.copy_calibration:
         copy_calibration()
-    t = time_workload(w, args.steps, args.warmup, args.settle)
+    t = time_workload(w, args.steps, args.warmup, args.settle, graph=args.graph)
     achieved, peak, ai = line_for(w, t, args.steps, args.warmup)
     value = w.flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
     traffic = traffic_for(w.name)
@@ -302,8 +336,9 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel_ms_mean": round(t["kernel_ms_mean"], 5),
-            "kernel_ms_p10_p50_p90": [round(t["kernel_ms_p10"], 5), round(t["kernel_ms_median"], 5),
-                                      round(t["kernel_ms_p90"], 5)],
+            "kernel_ms_p10_p50_p90": None if t["kernel_ms_p10"] is None else
+            [round(t["kernel_ms_p10"], 5), round(t["kernel_ms_median"], 5), round(t["kernel_ms_p90"], 5)],
+            "timing": t["timing"],
             "arith_intensity_flop_per_compulsory_byte": round(ai, 1),
             "hbm_ceiling_tflops": round(min(peak, ai * HBM_GBPS / 1e3), 1),
         },
@@ -313,7 +348,8 @@ def main():
         for ow in WORKLOADS:
             if ow.name == w.name:
                 continue
-            ot = time_workload(ow, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle)
+            ot = time_workload(ow, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle,
+                               graph=args.graph)
             oa, opk, oai = line_for(ow, ot, 0, 0)
             others[ow.name] = {"tflops_kernel": round(oa, 1), "pct_of_dense_peak": round(100 * oa / opk, 2),
                                "kernel_ms_median": round(ot["kernel_ms_median"], 4), "dtype": ow.dtype,
