@@ -11,6 +11,9 @@ Two independent implementations of the same result:
 * ``naive.attention_naive`` / ``naive.attention_rows`` -- the plain definition
   softmax(scale * Q K^T) V with an optional causal mask, two-pass stable
   softmax over each full row, plus the per-row logsumexp L.
+* ``gqa.attention_gqa`` -- grouped-query attention: each K/V head serves a
+  group of consecutive query heads; the plain definition applied per query
+  head against its group's K/V.
 * ``online.attention_online`` -- the blockwise online-softmax recurrence
   (running row max m, running row sum l, rescale of the partial output when m
   grows, one normalisation at the end), for any block sizes.
@@ -21,7 +24,8 @@ Every function here is pinned; none is "parity unpinned".
 """
 
 from .naive import attention_naive, attention_rows
+from .gqa import attention_gqa, expand_kv
 from .online import attention_online
 from .compare import errors
 
-__all__ = ["attention_naive", "attention_rows", "attention_online", "errors"]
+__all__ = ["attention_naive", "attention_rows", "attention_gqa", "expand_kv", "attention_online", "errors"]

@@ -22,7 +22,7 @@ import mpmath
 import numpy as np
 import pytest
 
-from oracle import attention_naive, attention_online, attention_rows
+from oracle import attention_gqa, attention_naive, attention_online, attention_rows
 
 
 def rand_qkv(N, d, seed, B=None, H=None, scale_inputs=1.0):
@@ -230,3 +230,69 @@ def test_pins_reject_planted_mistakes(mutant):
         "transpose_q": transpose_q,
     }
     assert not _pins_hold(fns[mutant])
+
+
+# ---------------------------------------------------------------- grouped-query attention
+def _gqa_pins_hold(fn):
+    """Pins of the grouping rule for an arbitrary (q, k, v, scale, causal) -> (O, L) over
+    q [B,H,N,d] and k, v [B,H_kv,N,d]: query head h must read K/V head h // (H / H_kv)."""
+    ok = True
+    rng = np.random.default_rng(5)
+    B, H, H_kv, N, d = 2, 6, 3, 7, 4
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H_kv, N, d))
+    # closed form: V constant per K/V head (value = 10*b + g + 1) -> every output row of a
+    # query head equals its own group's constant, whatever the weights
+    v = np.empty((B, H_kv, N, d))
+    for b in range(B):
+        for g in range(H_kv):
+            v[b, g] = 10 * b + g + 1
+    for causal in (False, True):
+        o, _ = fn(q, k, v, 0.7, causal)
+        for b in range(B):
+            for h in range(H):
+                ok &= np.max(np.abs(o[b, h] - (10 * b + h // (H // H_kv) + 1))) < 1e-12
+    # each query head against its group's K/V, by the single-head definition
+    v = rng.standard_normal((B, H_kv, N, d))
+    o, l = fn(q, k, v, 0.7, True)
+    for b in range(B):
+        for h in range(H):
+            g = h // (H // H_kv)
+            oh, lh = attention_rows(q[b, h], k[b, g], v[b, g], 0.7, True)
+            ok &= np.max(np.abs(o[b, h] - oh)) < 1e-12 and np.max(np.abs(l[b, h] - lh)) < 1e-12
+    return bool(ok)
+
+
+def test_gqa_pins_accept_oracle():
+    assert _gqa_pins_hold(lambda q, k, v, s, c: attention_gqa(q, k, v, s, c, threads=1))
+
+
+def test_gqa_with_all_heads_is_mha_and_mqa_shares_one_head():
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((1, 4, 9, 8)) for _ in range(3))
+    o1, l1 = attention_gqa(q, k, v, 0.4, True, threads=1)
+    o2, l2 = attention_naive(q, k, v, 0.4, True, threads=1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    o, l = attention_gqa(q, k[:, :1], v[:, :1], 0.4, False, threads=1)     # MQA
+    for h in range(4):
+        oh, lh = attention_rows(q[0, h], k[0, 0], v[0, 0], 0.4, False)
+        assert np.allclose(o[0, h], oh, rtol=0, atol=1e-13) and np.allclose(l[0, h], lh, rtol=0, atol=1e-13)
+    with pytest.raises(ValueError):
+        attention_gqa(q, k[:, :3], v[:, :3], 0.4, False)
+
+
+@pytest.mark.parametrize("mutant", ["interleaved", "last_group", "swap_kv"])
+def test_gqa_pins_reject_planted_mistakes(mutant):
+    def interleaved(q, k, v, s, c):               # h -> h % H_kv instead of h // G
+        H, H_kv = q.shape[1], k.shape[1]
+        idx = np.arange(H) % H_kv
+        return attention_naive(q, k[:, idx], v[:, idx], s, c, threads=1)
+
+    def last_group(q, k, v, s, c):                # every head reads the last K/V head
+        H, H_kv = q.shape[1], k.shape[1]
+        idx = np.full(H, H_kv - 1)
+        return attention_naive(q, k[:, idx], v[:, idx], s, c, threads=1)
+
+    fns = {"interleaved": interleaved, "last_group": last_group,
+           "swap_kv": lambda q, k, v, s, c: attention_gqa(q, v, k, s, c, threads=1)}
+    assert not _gqa_pins_hold(fns[mutant])

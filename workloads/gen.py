@@ -29,10 +29,20 @@ class Workload:
     causal: bool
     seed: int
     scale: float = None  # default 1/sqrt(d)
+    H_kv: int = None     # K/V heads (grouped-query attention); default H
 
     @property
     def softmax_scale(self):
         return 1.0 / math.sqrt(self.d) if self.scale is None else self.scale
+
+    @property
+    def kv_heads(self):
+        return self.H if self.H_kv is None else self.H_kv
+
+    @property
+    def group(self):
+        """Query heads per K/V head; query head h reads K/V head h // group."""
+        return self.H // self.kv_heads
 
     @property
     def flops(self):
@@ -52,7 +62,8 @@ class Workload:
     def compulsory_bytes(self):
         """Q, K, V read once; O and the fp32 logsumexp written once."""
         n = self.B * self.H * self.N
-        return 3 * n * self.d * self.elem_bytes + n * self.d * self.out_elem_bytes + 4 * n
+        nkv = self.B * self.kv_heads * self.N
+        return (n + 2 * nkv) * self.d * self.elem_bytes + n * self.d * self.out_elem_bytes + 4 * n
 
     def with_(self, **kw):
         return replace(self, **kw)
@@ -65,6 +76,8 @@ WORKLOADS = [
     Workload("long_causal_bf16_b1h32n8192d128", 1, 32, 8192, 128, "bf16", True, seed=4),
     Workload("wide_bf16_b2h8n16384d256", 2, 8, 16384, 256, "bf16", False, seed=5),
     Workload("wide_fp8_b2h8n16384d256", 2, 8, 16384, 256, "fp8", False, seed=5),
+    # grouped-query attention: 32 query heads over 8 K/V heads, long causal context
+    Workload("gqa_causal_bf16_b1h32kv8n8192d128", 1, 32, 8192, 128, "bf16", True, seed=6, H_kv=8),
 ]
 
 
@@ -77,7 +90,8 @@ def by_name(name):
 
 @dataclass
 class AttnInputs:
-    """Storage-format tensors [B,H,N,d] plus their exact float64 meaning.
+    """Storage-format tensors plus their exact float64 meaning: q [B,H,N,d],
+    k and v [B,H_kv,N,d] (H_kv = H unless the workload groups query heads).
 
     q/k/v hold float32 values (f32), uint16 bf16 bits (bf16) or uint8 e4m3fn
     bits (fp8).  ``descale`` is (s_q, s_k, s_v): the value of an fp8 element is
@@ -90,7 +104,8 @@ class AttnInputs:
     descale: tuple = (1.0, 1.0, 1.0)
 
     def f64(self, which, b=None, h=None):
-        """float64 values of q, k or v (optionally one (b, h) slice) exactly as the kernel sees them."""
+        """float64 values of q, k or v (optionally one (b, h) slice; h indexes that tensor's own
+        heads) exactly as the kernel sees them."""
         x = getattr(self, which)
         if b is not None:
             x = x[b, h]
@@ -103,12 +118,12 @@ class AttnInputs:
         return e4m3fn_bits_to_f64(x) * float(self.descale[s])
 
 
-def _draw(B, H, N, d, seed):
+def _draw(B, H, N, d, seed, H_kv=None):
     rng = np.random.default_rng(seed)
-    shape = (B, H, N, d)
-    q = rng.standard_normal(shape, dtype=np.float32)
-    k = rng.standard_normal(shape, dtype=np.float32)
-    v = rng.standard_normal(shape, dtype=np.float32)
+    kv_shape = (B, H if H_kv is None else H_kv, N, d)
+    q = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    k = rng.standard_normal(kv_shape, dtype=np.float32)
+    v = rng.standard_normal(kv_shape, dtype=np.float32)
     return q, k, v
 
 
@@ -123,7 +138,7 @@ def quantize_e4m3_per_tensor(x32):
 def make_inputs(w, seed=None):
     """Draw the inputs of workload ``w`` (optionally with another seed)."""
     seed = w.seed if seed is None else seed
-    q, k, v = _draw(w.B, w.H, w.N, w.d, seed)
+    q, k, v = _draw(w.B, w.H, w.N, w.d, seed, w.kv_heads)
     if w.dtype == "f32":
         return AttnInputs(w, q, k, v)
     qb, kb, vb = bf16_bits_from_f32(q), bf16_bits_from_f32(k), bf16_bits_from_f32(v)
