@@ -99,10 +99,13 @@ def time_workload(w, steps, warmup, settle_s=0.25, graph=False):
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=out_dtype, device="cuda")
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
     # stream=None: the current stream at call time (the capture stream while capturing)
+    gqa = w.kv_heads != w.H
     if w.dtype == "fp8":
-        launch = lambda: fa.fa_fwd_fp8(q, k, v, *x.descale, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+        f = fa.fa_fwd_gqa_fp8 if gqa else fa.fa_fwd_fp8
+        launch = lambda: f(q, k, v, *x.descale, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
     else:
-        launch = lambda: fa.fa_fwd(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+        f = fa.fa_fwd_gqa if gqa else fa.fa_fwd
+        launch = lambda: f(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
     # untimed: let the clocks settle on this very step, then the W warmup steps
     torch.cuda.synchronize()
     t_end = time.perf_counter() + settle_s

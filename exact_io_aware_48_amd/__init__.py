@@ -6,7 +6,9 @@ C ABI and this package binds it with the same names.
 """
 
 from ._lib import FA_BF16, FA_F32, FA_FP8_E4M3, LIB_PATH
-from .api import FaError, fa_fwd, fa_fwd_fp8, fa_plan, fa_status_string, fa_version
+from .api import (FaError, fa_fwd, fa_fwd_fp8, fa_fwd_gqa, fa_fwd_gqa_fp8, fa_plan, fa_status_string,
+                  fa_version)
 
-__all__ = ["fa_fwd", "fa_fwd_fp8", "fa_plan", "fa_status_string", "fa_version", "FaError",
+__all__ = ["fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_plan", "fa_status_string", "fa_version",
+           "FaError",
            "FA_F32", "FA_BF16", "FA_FP8_E4M3", "LIB_PATH"]

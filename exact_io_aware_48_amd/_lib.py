@@ -24,6 +24,10 @@ def load():
     lib.fa_fwd.restype = i32
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, f32, f32, i32, vp]
     lib.fa_fwd_fp8.restype = i32
+    lib.fa_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.fa_fwd_gqa.restype = i32
+    lib.fa_fwd_gqa_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, f32, f32, f32, i32, vp]
+    lib.fa_fwd_gqa_fp8.restype = i32
     pi, pl = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)
     lib.fa_plan.argtypes = [i64, i64, i64, i64, i32, i32, pi, pi, pl, pi, pi, pl]
     lib.fa_plan.restype = i32

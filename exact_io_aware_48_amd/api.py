@@ -109,3 +109,59 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, sc
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_fp8")
     return o, lse
+
+
+def _gqa_shapes(q, k, v, names):
+    B, H, N, d = q.shape
+    if k.shape != v.shape or k.dim() != 4 or k.shape[0] != B or k.shape[2] != N or k.shape[3] != d:
+        raise ValueError(f"{names[1]} and {names[2]} must both be [B, H_kv, N, d] with q's B, N and d")
+    H_kv = k.shape[1]
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"{H} query heads do not split into groups over {H_kv} K/V heads")
+    return B, H, H_kv, N, d
+
+
+def fa_fwd_gqa(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None):
+    """Grouped-query attention: q [B, H, N, d], k and v [B, H_kv, N, d]; query head h
+    attends over K/V head h // (H / H_kv).  Same dtypes, outputs and options as fa_fwd."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm)
+    if q.dtype in _FP8_DTYPES:
+        return fa_fwd_gqa_fp8(q, k, v, 1.0, 1.0, 1.0, o=o, lse=lse, scale=scale, causal=causal, stream=stream)
+    if q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"unsupported dtypes {q.dtype}/{k.dtype}/{v.dtype}")
+    B, H, H_kv, N, d = _gqa_shapes(q, k, v, ("q", "k", "v"))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                B, H, H_kv, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
+                                _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_gqa")
+    return o, lse
+
+
+def fa_fwd_gqa_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, scale=None, causal=False,
+                   stream=None):
+    """fa_fwd_gqa on FP8 (OCP e4m3fn) inputs with per-tensor descales; bfloat16 O, float32 lse."""
+    for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check(t, nm)
+        if t.dtype not in _FP8_DTYPES:
+            raise ValueError(f"{nm} must be float8_e4m3fn or uint8 bytes")
+    B, H, H_kv, N, d = _gqa_shapes(q8, k8, v8, ("q8", "k8", "v8"))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    st = _lib.load().fa_fwd_gqa_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                    B, H, H_kv, N, d, float(scale), float(q_descale), float(k_descale),
+                                    float(v_descale), int(bool(causal)), _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_gqa_fp8")
+    return o, lse

@@ -134,10 +134,11 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
 }
 
 fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-              int64_t N, int64_t d, float scale, float dq, float dk, float dv, int causal, int dtype,
-              void* stream) {
+              int64_t H_kv, int64_t N, int64_t d, float scale, float dq, float dk, float dv, int causal,
+              int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   fa_status st = check_shape(B, H, N, d, dtype);
+  if (st == FA_OK && (H_kv < 1 || H % H_kv != 0)) st = FA_ERR_SHAPE;
   if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
@@ -152,7 +153,8 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.BH = (int)(B * H);
   p.N = (int)N;
   p.nrb = (int)((N + br - 1) / br);
-  p.xcd_heads = (p.BH % 8 == 0) ? 1 : 0;
+  p.G = (int)(H / H_kv);
+  p.xcd_heads = ((p.BH / p.G) % 8 == 0) ? 1 : 0;   // whole groups of heads per XCD
   const double c2 = std::fabs((double)scale) * (double)dq * (double)dk * 1.4426950408889634;
   if (!std::isfinite((float)c2)) return FA_ERR_SCALE;
   // The kernel masks scores with -inf and relies on c2 > 0 to keep their
@@ -180,14 +182,26 @@ extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                  int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
-  return run(q, k, v, o, lse, B, H, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream);
+  return run(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream);
 }
 
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int64_t B,
                      int64_t H, int64_t N, int64_t d, float scale, float q_descale, float k_descale,
                      float v_descale, int causal, void* stream) {
-  return run(q8, k8, v8, o_bf16, lse, B, H, N, d, scale, q_descale, k_descale, v_descale, causal, FA_FP8_E4M3,
-             stream);
+  return run(q8, k8, v8, o_bf16, lse, B, H, H, N, d, scale, q_descale, k_descale, v_descale, causal,
+             FA_FP8_E4M3, stream);
+}
+
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t H_kv, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  return run(q, k, v, o, lse, B, H, H_kv, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream);
+}
+
+fa_status fa_fwd_gqa_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, int64_t B,
+                         int64_t H, int64_t H_kv, int64_t N, int64_t d, float scale, float q_descale,
+                         float k_descale, float v_descale, int causal, void* stream) {
+  return run(q8, k8, v8, o_bf16, lse, B, H, H_kv, N, d, scale, q_descale, k_descale, v_descale, causal,
+             FA_FP8_E4M3, stream);
 }
 
 fa_status fa_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int dtype, int* block_rows,
@@ -219,7 +233,8 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H, N must be >= 1 and sizes must fit the index types";
+    case FA_ERR_SHAPE:
+      return "FA_ERR_SHAPE: B, H, N (and H_kv) must be >= 1, H a multiple of H_kv, and sizes must fit the index types";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64, 128 or 256 and dtype a fa_dtype value";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and descales finite and > 0";

@@ -20,7 +20,8 @@ struct Params {
   int BH;          // batch * heads
   int N;           // sequence length (queries = keys)
   int nrb;         // row blocks per head = ceil(N / B_r)
-  int xcd_heads;   // 1: heads are spread over XCDs head-major (BH % 8 == 0)
+  int G;           // query heads per K/V head (grouped-query attention; 1 = one K/V head per head)
+  int xcd_heads;   // 1: K/V heads are spread over XCDs, with their query heads ((BH / G) % 8 == 0)
   int cus_per_xcd; // compute units per XCD (0: unknown)
   int zigzag;      // causal grid fully resident: deal row blocks to CUs zig-zag (see map_block)
   float c2;        // |scale| * descale_q * descale_k * log2(e)
@@ -172,8 +173,9 @@ __device__ __forceinline__ void split8(const float* x, i32x4& hi, i32x4& lo) {
 // The hardware deals workgroup ids to the 8 XCDs round-robin (XCD = id % 8)
 // and, within an XCD, slots s = id / 8 to its CUs round-robin (CU s % C for
 // C CUs per XCD), so slots s, s + C, s + 2C ... share a CU.
-//   * xcd_heads: all row blocks of a head stay on one XCD (its K/V stream
-//     stays in that XCD's L2).
+//   * xcd_heads: all row blocks of all query heads that share a K/V head
+//     stay on one XCD (that K/V stream stays in the XCD's L2): K/V head
+//     xcd + 8*j, and the XCD-local query head hl is query head G*(xcd + 8*(hl/G)) + hl%G.
 //   * causal: row blocks differ in work (row block i has i+1 key tiles of
 //     B_r), so the XCD's work list is ordered heaviest first.  When the whole
 //     grid is resident at once (zigzag), consecutive rounds of C slots take
@@ -185,13 +187,16 @@ __device__ __forceinline__ int zigzag_slot(int s, int total, int C) {
   const int R = min(C, total - base);          // slots in this round
   return base + ((r & 1) ? R - 1 - pos : pos);
 }
+__device__ __forceinline__ int xcd_head(const Params& p, int xcd, int hl) {
+  return p.G * (xcd + 8 * (hl / p.G)) + hl % p.G;
+}
 template <bool CAUSAL>
 __device__ __forceinline__ void map_block(const Params& p, int id, int& bh, int& rb) {
   const int nrb = p.nrb;
   if constexpr (!CAUSAL) {
     if (p.xcd_heads) {
       const int xcd = id & 7, s = id >> 3;
-      bh = xcd + 8 * (s / nrb);
+      bh = xcd_head(p, xcd, s / nrb);
       rb = s % nrb;
     } else {
       bh = id % p.BH;
@@ -201,7 +206,7 @@ __device__ __forceinline__ void map_block(const Params& p, int id, int& bh, int&
     if (p.xcd_heads) {
       const int xcd = id & 7, s = id >> 3, hpx = p.BH >> 3;
       const int k = p.zigzag ? zigzag_slot(s, hpx * nrb, p.cus_per_xcd) : s;
-      bh = xcd + 8 * (k % hpx);
+      bh = xcd_head(p, xcd, k % hpx);
       rb = nrb - 1 - k / hpx;
     } else {
       const int k = p.zigzag ? zigzag_slot(id, p.BH * nrb, 8 * p.cus_per_xcd) : id;

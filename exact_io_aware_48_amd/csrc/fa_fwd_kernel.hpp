@@ -77,7 +77,8 @@ void fa_fwd_kernel(Params p) {
   int bh, rb;
   map_block<CAUSAL>(p, blockIdx.x, bh, rb);
   const int N = p.N;
-  const int64_t head_off = (int64_t)bh * N * D;    // element offset of this head
+  const int64_t head_off = (int64_t)bh * N * D;    // element offset of this head in Q and O
+  const int64_t kv_off = (int64_t)(bh / p.G) * N * D;   // ... and of its K/V head
   const int q_row0 = rb * G::BR;                   // first query of the workgroup
   const int qw0 = q_row0 + 32 * wave;              // first query of this wave
   const int my_q = qw0 + ln.n;
@@ -99,8 +100,8 @@ void fa_fwd_kernel(Params p) {
     kstage.init(wave, lane);
     vstage.init(wave, lane);
   }
-  const char* kglob = static_cast<const char*>(p.k) + head_off * G::EB;
-  const char* vglob = static_cast<const char*>(p.v) + head_off * G::EB;
+  const char* kglob = static_cast<const char*>(p.k) + kv_off * G::EB;
+  const char* vglob = static_cast<const char*>(p.v) + kv_off * G::EB;
   auto issue_tile = [&](int j, char FA_LDS* kdst, char FA_LDS* vdst) __attribute__((always_inline)) {
     kstage.issue(kglob, j, N, kdst, wave, lane);
     vstage.issue(vglob, j, N, vdst, wave, lane);
@@ -114,8 +115,8 @@ void fa_fwd_kernel(Params p) {
       const int u = tid + i * G::NT;
       const int row = u / G::CPR, ch = u % G::CPR;
       const bool ok = row0 + row < N;
-      const float* kb = static_cast<const float*>(p.k) + head_off + (int64_t)(row0 + row) * D + ch * 8;
-      const float* vb = static_cast<const float*>(p.v) + head_off + (int64_t)(row0 + row) * D + ch * 8;
+      const float* kb = static_cast<const float*>(p.k) + kv_off + (int64_t)(row0 + row) * D + ch * 8;
+      const float* vb = static_cast<const float*>(p.v) + kv_off + (int64_t)(row0 + row) * D + ch * 8;
       kst[2 * i] = ok ? *reinterpret_cast<const i32x4*>(kb) : i32x4{0, 0, 0, 0};
       kst[2 * i + 1] = ok ? *reinterpret_cast<const i32x4*>(kb + 4) : i32x4{0, 0, 0, 0};
       vst[2 * i] = ok ? *reinterpret_cast<const i32x4*>(vb) : i32x4{0, 0, 0, 0};

@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or an element count overflows int64/int32 indexing */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, H_kv < 1 or not dividing H, or an element count overflows int64/int32 indexing */
   FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128, 256}, or unknown dtype */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   FA_ERR_SCALE = 5,       /* scale not finite, or an fp8 descale not finite and > 0 */
@@ -96,7 +96,32 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf1
                      int causal, void* stream);
 
 /*
- * fa_plan -- the launch fa_fwd / fa_fwd_fp8 would make for this problem,
+ * fa_fwd_gqa -- grouped-query attention: the H query heads are split into
+ * H_kv consecutive groups of G = H / H_kv heads and every query head h of
+ * group h / G attends over K/V head h / G (multi-query attention is
+ * H_kv = 1; H_kv = H is fa_fwd).  Otherwise the same operation, arguments,
+ * errors and guarantees as fa_fwd.  The pages name Multi-Query Attention
+ * among the architectures FlashAttention-2 extended its support to
+ * (systems-analysis.info "FlashAttention (PL)", section "FlashAttention-2
+ * (2023)"); grouped-query attention is read as its general case.
+ *   q, o   : [B][H][N][d]
+ *   k, v   : [B][H_kv][N][d]
+ *   lse    : float32 [B][H][N]
+ *   H_kv   : >= 1 and dividing H, else FA_ERR_SHAPE
+ */
+fa_status fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                     float scale, int causal, int dtype, void* stream);
+
+/* fa_fwd_gqa on FP8 inputs with per-tensor descales, as fa_fwd_fp8. */
+fa_status fa_fwd_gqa_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, float scale,
+                         float q_descale, float k_descale, float v_descale,
+                         int causal, void* stream);
+
+/*
+ * fa_plan -- the launch fa_fwd / fa_fwd_fp8 (and their grouped-query
+ * forms, whose grid does not depend on H_kv) would make for this problem,
  * without launching anything.  Any output pointer may be NULL.
  *   block_rows / block_cols : queries per workgroup (B_r) and keys per K/V tile (B_c)
  *   workgroups, threads     : grid size and threads per workgroup

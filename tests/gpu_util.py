@@ -32,7 +32,12 @@ def run_gpu(x: AttnInputs, stream=None, scale=None):
     w = x.workload
     q, k, v = to_device(x)
     scale = w.softmax_scale if scale is None else scale
-    if w.dtype == "fp8":
+    if w.kv_heads != w.H:                         # grouped-query attention
+        if w.dtype == "fp8":
+            o, lse = fa.fa_fwd_gqa_fp8(q, k, v, *x.descale, scale=scale, causal=w.causal, stream=stream)
+        else:
+            o, lse = fa.fa_fwd_gqa(q, k, v, scale=scale, causal=w.causal, stream=stream)
+    elif w.dtype == "fp8":
         o, lse = fa.fa_fwd_fp8(q, k, v, *x.descale, scale=scale, causal=w.causal, stream=stream)
     else:
         o, lse = fa.fa_fwd(q, k, v, scale=scale, causal=w.causal, stream=stream)
@@ -47,7 +52,8 @@ def oracle_full(x: AttnInputs, scale=None):
     l = np.empty((w.B, w.H, w.N))
     for b in range(w.B):
         for h in range(w.H):
-            o[b, h], l[b, h] = attention_rows(x.f64("q", b, h), x.f64("k", b, h), x.f64("v", b, h), scale, w.causal)
+            g = h // w.group                         # the K/V head of query head h
+            o[b, h], l[b, h] = attention_rows(x.f64("q", b, h), x.f64("k", b, g), x.f64("v", b, g), scale, w.causal)
     return o, l
 
 

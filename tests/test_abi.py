@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_plan", "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_plan",
+                                    "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -72,6 +73,21 @@ def test_fa_fwd_validation(lib, args, expected):
                                                 ((1.0, 1.0, float("nan")), 5), ((1.0, float("inf"), 1.0), 5)])
 def test_fa_fwd_fp8_descale_validation(lib, descales, expected):
     assert lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 64, 0.1, *descales, 0, None) == expected
+
+
+@pytest.mark.parametrize("H,H_kv,expected", [(8, 0, 2), (8, -2, 2), (8, 3, 2), (6, 4, 2), (4, 8, 2)])
+def test_fa_fwd_gqa_group_validation(lib, H, H_kv, expected):
+    assert lib.fa_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, H_kv, 64, 64, 0.1, 0, 1, None) == expected
+    assert lib.fa_fwd_gqa_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, H_kv, 64, 64, 0.1, 1.0, 1.0, 1.0, 0,
+                              None) == expected
+
+
+def test_fa_fwd_gqa_checks_the_rest_like_fa_fwd(lib):
+    # a valid grouping still gets every other check of fa_fwd, before any launch
+    assert lib.fa_fwd_gqa(0, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 64, 0.1, 0, 1, None) == 1
+    assert lib.fa_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 96, 0.1, 0, 1, None) == 3
+    assert lib.fa_fwd_gqa(FAKE, FAKE + 8, FAKE, FAKE, FAKE, 1, 8, 2, 64, 64, 0.1, 0, 1, None) == 4
+    assert lib.fa_fwd_gqa_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, 64, 0.1, 1.0, 0.0, 1.0, 0, None) == 5
 
 
 def test_fp8_scale_overflow_rejected(lib):

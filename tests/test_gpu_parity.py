@@ -36,6 +36,13 @@ REDUCED = [
     ("wide_bf16_b2h8n16384d256", 1, 2, 700),
     ("wide_fp8_b2h8n16384d256", 1, 2, 700),
 ]
+# grouped-query: (base workload, B, H, H_kv, N)
+REDUCED_GQA = [
+    ("gqa_causal_bf16_b1h32kv8n8192d128", 1, 8, 2, 700),     # groups of 4
+    ("gqa_causal_bf16_b1h32kv8n8192d128", 2, 6, 3, 333),     # groups of 2, two batches
+    ("gqa_causal_bf16_b1h32kv8n8192d128", 1, 4, 1, 300),     # MQA
+    ("gqa_causal_bf16_b1h32kv8n8192d128", 1, 16, 8, 257),    # 8 K/V heads: one per XCD
+]
 
 
 @pytest.mark.parametrize("name,B,H,N", REDUCED)
@@ -47,6 +54,18 @@ def test_reduced_workloads_all_elements(name, B, H, N):
     o_ref, l_ref = oracle_full(x)
     e = errors(o, o_ref, l, l_ref)
     check(e, w.dtype, f"{name} B={B} H={H} N={N}")
+
+
+@pytest.mark.parametrize("name,B,H,H_kv,N", REDUCED_GQA)
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("bf16", 256, False),
+                                            ("fp8", 128, True), ("f32", 64, True)])
+def test_gqa_all_elements(name, B, H, H_kv, N, dtype, d, causal):
+    w = by_name(name).with_(B=B, H=H, H_kv=H_kv, N=N, d=d, dtype=dtype, causal=causal)
+    _print_case("gqa", name, B, H, H_kv, N, dtype, d, causal)
+    x = make_inputs(w)
+    o, l = run_gpu(x)
+    o_ref, l_ref = oracle_full(x)
+    check(errors(o, o_ref, l, l_ref), dtype, f"gqa B={B} H={H} H_kv={H_kv} N={N} {dtype} d={d} causal={causal}")
 
 
 # ---------------------------------------------------------------- edge shapes
@@ -82,7 +101,8 @@ def test_full_size_workloads(name):
     og, orf, lg, lrf = [], [], [], []
     for b, h in heads:
         rows = sample_rows(w.N, seed=b * 131 + h)
-        r_o, r_l = attention_rows(x.f64("q", b, h), x.f64("k", b, h), x.f64("v", b, h), w.softmax_scale,
+        g = h // w.group
+        r_o, r_l = attention_rows(x.f64("q", b, h), x.f64("k", b, g), x.f64("v", b, g), w.softmax_scale,
                                   w.causal, rows)
         og.append(o[b, h, rows]); orf.append(r_o); lg.append(l[b, h, rows]); lrf.append(r_l)
     e = errors(np.concatenate(og), np.concatenate(orf), np.concatenate(lg), np.concatenate(lrf))
