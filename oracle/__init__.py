@@ -15,7 +15,8 @@ Two independent implementations of the same result:
   group of consecutive query heads; the plain definition applied per query
   head against its group's K/V.
 * ``backward.attention_backward`` -- dQ, dK, dV of the scalar loss sum(dO * O),
-  the chain rule of the plain definition written out (with grouped K/V heads).
+  the chain rule of the plain definition written out (with grouped K/V heads);
+  ``dq_rows`` / ``dkdv_cols`` restrict it to chosen query rows or keys.
 * ``online.attention_online`` -- the blockwise online-softmax recurrence
   (running row max m, running row sum l, rescale of the partial output when m
   grows, one normalisation at the end), for any block sizes.
@@ -28,8 +29,8 @@ Every function here is pinned; none is "parity unpinned".
 from .naive import attention_naive, attention_rows
 from .gqa import attention_gqa, expand_kv
 from .online import attention_online
-from .backward import attention_backward, backward_head, delta_rows
+from .backward import attention_backward, backward_head, delta_rows, dkdv_cols, dq_rows
 from .compare import errors
 
 __all__ = ["attention_naive", "attention_rows", "attention_gqa", "expand_kv", "attention_online",
-           "attention_backward", "backward_head", "delta_rows", "errors"]
+           "attention_backward", "backward_head", "delta_rows", "dq_rows", "dkdv_cols", "errors"]

@@ -19,8 +19,13 @@ loss  sum(dO * O)  whose gradient a training step propagates:
 Grouped-query attention (K/V head g serving query heads g*G .. g*G+G-1): dK
 and dV of a K/V head are the sums over the query heads of its group.
 
+For large heads, ``dq_rows`` gives dQ of chosen query rows and ``dkdv_cols``
+dK, dV of chosen keys, from the same formulas restricted to those rows or
+columns of S (each still sees its whole softmax row).
+
 Pins (tests/test_oracle_backward.py): central finite differences of the
-forward oracle, closed forms and invariants, planted mistakes.
+forward oracle, closed forms and invariants, planted mistakes; the restricted
+forms agree with ``backward_head`` on every row and key.
 """
 
 import numpy as np
@@ -81,3 +86,52 @@ def attention_backward(q, k, v, do, scale, causal, row_chunk=1024):
 def delta_rows(o, do):
     """D = rowsum(dO * O) per query row, the quantity the backward precomputes ([..., N])."""
     return np.sum(np.asarray(o, dtype=np.float64) * np.asarray(do, dtype=np.float64), axis=-1)
+
+
+def _masked_scores(q, k, scale, causal, rows, cols):
+    s = scale * (q[rows] @ k[cols].T)
+    if causal:
+        s = np.where(cols[None, :] > rows[:, None], -np.inf, s)
+    return s
+
+
+def _row_stats(q, k, v, do, scale, causal, rows):
+    """Row max m, row sum l (so L = m + log l), O rows and D rows for the given query rows."""
+    cols = np.arange(k.shape[0])
+    s = _masked_scores(q, k, scale, causal, rows, cols)
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    l = p.sum(axis=1)
+    o = (p / l[:, None]) @ v
+    return m, l, o, np.sum(do[rows] * o, axis=1)
+
+
+def dq_rows(q, k, v, do, scale, causal, rows):
+    """dQ [len(rows), d] of one head for the given query rows (float64)."""
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.arange(k.shape[0])
+    s = _masked_scores(q, k, scale, causal, rows, cols)
+    m, l, _, D = _row_stats(q, k, v, do, scale, causal, rows)
+    p = np.exp(s - m[:, None]) / l[:, None]
+    ds = p * (do[rows] @ v.T - D[:, None])
+    return scale * (ds @ k)
+
+
+def dkdv_cols(q, k, v, do, scale, causal, keys, row_chunk=1024):
+    """dK, dV [len(keys), d] of one head for the given keys (float64): the
+    softmax statistics of every query row, then the keys' columns of P and dS."""
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    keys = np.asarray(keys, dtype=np.int64)
+    N = q.shape[0]
+    dk = np.zeros((len(keys), q.shape[1]))
+    dv = np.zeros_like(dk)
+    for r0 in range(0, N, row_chunk):
+        rows = np.arange(r0, min(r0 + row_chunk, N))
+        m, l, _, D = _row_stats(q, k, v, do, scale, causal, rows)
+        s = _masked_scores(q, k, scale, causal, rows, keys)
+        p = np.exp(s - m[:, None]) / l[:, None]
+        ds = p * (do[rows] @ v[keys].T - D[:, None])
+        dv += p.T @ do[rows]
+        dk += scale * (ds.T @ q[rows])
+    return dk, dv

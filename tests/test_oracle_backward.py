@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import attention_gqa
-from oracle.backward import attention_backward, backward_head, delta_rows
+from oracle.backward import attention_backward, backward_head, delta_rows, dkdv_cols, dq_rows
 
 SCALE = 0.7
 
@@ -158,3 +158,16 @@ def test_backward_head_rows_in_chunks_equal_whole():
     b = backward_head(q, k, v, do, 0.3, True, row_chunk=1024)
     for x, y in zip(a, b):
         assert np.allclose(x, y, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_restricted_forms_agree_with_whole_head(causal):
+    rng = np.random.default_rng(21)
+    N, d = 45, 6
+    q, k, v, do = (rng.standard_normal((N, d)) for _ in range(4))
+    dq, dk, dv = backward_head(q, k, v, do, 0.4, causal)
+    rows = np.array([0, 1, 7, 30, 44])
+    assert np.allclose(dq_rows(q, k, v, do, 0.4, causal, rows), dq[rows], rtol=0, atol=1e-12)
+    keys = np.array([0, 3, 22, 44])
+    a, b = dkdv_cols(q, k, v, do, 0.4, causal, keys, row_chunk=8)
+    assert np.allclose(a, dk[keys], rtol=0, atol=1e-12) and np.allclose(b, dv[keys], rtol=0, atol=1e-12)

@@ -168,3 +168,12 @@ def from_f32(w, q, k, v):
         outs.append(bits)
         scales.append(s)
     return AttnInputs(w, outs[0], outs[1], outs[2], tuple(scales))
+
+
+def make_grad_output(w, seed=None):
+    """Upstream gradient dO [B, H, N, d] for the backward pass, as bf16 bits:
+    ``standard_normal`` float32 from ``default_rng(seed + 7919)`` (a stream
+    apart from the workload's Q, K, V), rounded to bfloat16."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed + 7919)
+    return bf16_bits_from_f32(rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32))
