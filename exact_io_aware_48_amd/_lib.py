@@ -1,4 +1,4 @@
-"""ctypes view of libfa_fwd.so: the C ABI declared in include/fa_fwd.h, nothing else."""
+"""ctypes view of libfa_fwd.so: the C ABI declared in include/fa_fwd.h and include/fa_bwd.h, nothing else."""
 
 import ctypes
 import os
@@ -33,6 +33,10 @@ def load():
     lib.fa_plan.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, pl]
+    lib.fa_bwd_workspace_size.restype = i32
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.fa_bwd.restype = i32
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i32
     _lib = lib

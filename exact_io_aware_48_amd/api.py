@@ -1,7 +1,8 @@
-"""Python binding of the C ABI (include/fa_fwd.h), same names, argument marshalling only.
+"""Python binding of the C ABI (include/fa_fwd.h, include/fa_bwd.h), same names,
+argument marshalling only.
 
 torch supplies device memory and streams; every step of the attention forward
-runs in the HIP kernels of libfa_fwd.so.  There is no fallback: if the library
+and backward runs in the HIP kernels of libfa_fwd.so.  There is no fallback: if the library
 is missing or a call fails, these functions raise.
 """
 
@@ -165,3 +166,51 @@ def fa_fwd_gqa_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_gqa_fp8")
     return o, lse
+
+
+def fa_bwd_workspace_size(B, H, N):
+    """Bytes of workspace fa_bwd needs (no GPU needed)."""
+    n = ctypes.c_int64()
+    st = _lib.load().fa_bwd_workspace_size(B, H, N, ctypes.byref(n))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_bwd_workspace_size")
+    return n.value
+
+
+def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
+           stream=None):
+    """dQ, dK, dV of attention, recomputing P from q, k and the forward's lse.
+
+    q, o, do: contiguous bfloat16 [B, H, N, d]; k, v: bfloat16 [B, H_kv, N, d]
+    (H_kv dividing H); lse: float32 [B, H, N] from the forward.  dq, dk, dv:
+    optional float32 outputs shaped like q, k, v; workspace: optional device
+    buffer of at least fa_bwd_workspace_size(B, H, N) bytes.  Returns (dq, dk, dv).
+    """
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, nm)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    B, H, H_kv, N, d = _gqa_shapes(q, k, v, ("q", "k", "v"))
+    if o.shape != q.shape or do.shape != q.shape:
+        raise ValueError("o and do must have q's shape")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    need = fa_bwd_workspace_size(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds fewer than {need} bytes")
+    st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            workspace.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
+                            float(scale), int(bool(causal)), _lib.FA_BF16, _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv

@@ -18,8 +18,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_fwd.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "fa_api.hip")]
-HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp")] + [os.path.join(INCLUDE, "fa_fwd.h")]
+SOURCES = [os.path.join(CSRC, "fa_api.hip"), os.path.join(CSRC, "fa_bwd_api.hip")]
+HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp",
+                                           "fa_host.hpp")] + [os.path.join(INCLUDE, h) for h in ("fa_fwd.h", "fa_bwd.h")]
 
 
 def hipcc():

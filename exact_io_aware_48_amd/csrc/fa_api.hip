@@ -11,6 +11,7 @@
 
 #include "fa_fwd.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_host.hpp"
 
 namespace {
 
@@ -61,34 +62,6 @@ Tile lookup_tile(int mode, int d) {
   }
 }
 
-// How many workgroups of `kern` the current device keeps resident at once,
-// and its CUs per XCD (0 when the CU count is not a multiple of the 8 XCDs).
-// Queried once per kernel and device and cached: the values never change.
-constexpr int kMaxDevices = 64;
-struct Residency {
-  int resident;
-  int cus_per_xcd;
-};
-Residency residency(const void* kern, int threads, std::atomic<int>* cache) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return {0, 0};
-  }
-  int packed = cache[dev].load(std::memory_order_relaxed);
-  if (packed == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) {
-      (void)hipGetLastError();
-      return {0, 0};
-    }
-    packed = (cus * per_cu) * 1024 + (cus % 8 == 0 ? cus / 8 : 0) + 1;   // + 1: never 0 once known
-    cache[dev].store(packed, std::memory_order_relaxed);
-  }
-  return {(packed - 1) / 1024, (packed - 1) % 1024};
-}
-
 template <int MODE, int D, bool CAUSAL>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
   using C = Cfg<MODE, D>;
@@ -111,8 +84,6 @@ hipError_t dispatch_d(const Params& p, int d, bool causal, int grid, hipStream_t
   if (d == 128) return causal ? launch<MODE, 128, true>(p, grid, s) : launch<MODE, 128, false>(p, grid, s);
   return causal ? launch<MODE, 256, true>(p, grid, s) : launch<MODE, 256, false>(p, grid, s);
 }
-
-bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 int mode_of(int dtype) {
   return dtype == FA_BF16 ? fa::MODE_BF16 : dtype == FA_FP8_E4M3 ? fa::MODE_FP8 : fa::MODE_F32;

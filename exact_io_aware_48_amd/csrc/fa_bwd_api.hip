@@ -1,0 +1,150 @@
+// C ABI of the FlashAttention backward (declared in include/fa_bwd.h):
+// argument checks, kernel instances, grids and the three launches.  No
+// allocation, no synchronisation, no state; the caller provides the
+// statistics workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa_bwd.h"
+#include "fa_bwd_kernel.hpp"
+#include "fa_host.hpp"
+
+namespace {
+
+using fa::BwdParams;
+
+// Shapes per head dim.  dK/dV: NW waves of 32 keys, each holding K, V and
+// the two fp32 accumulators in VGPRs (d = 128 needs more than 256 VGPRs, so
+// one wave per SIMD).  dQ: NW waves of 32 queries, B_c-key K/V tiles.
+template <int D> struct BwdCfg;
+template <> struct BwdCfg<64> {
+  static constexpr int KV_NW = 4, KV_WPE = 2;
+  static constexpr int Q_BC = 64, Q_NW = 4, Q_WPE = 2;
+};
+template <> struct BwdCfg<128> {
+  static constexpr int KV_NW = 4, KV_WPE = 1;
+  static constexpr int Q_BC = 64, Q_NW = 8, Q_WPE = 2;
+};
+
+int64_t stat_tiles(int64_t N) { return (N + fa::kStatRows - 1) / fa::kStatRows; }
+
+// A causal grid's workgroups are dealt zig-zag over the CUs when the whole
+// grid is resident at once (see map_block).
+template <bool CAUSAL>
+void set_balance(BwdParams& p, const void* kern, int threads, int grid, std::atomic<int>* cache) {
+  if constexpr (CAUSAL) {
+    const Residency r = residency(kern, threads, cache);
+    p.cus_per_xcd = r.cus_per_xcd;
+    p.zigzag = r.cus_per_xcd > 0 && grid <= r.resident ? 1 : 0;
+  } else {
+    (void)kern; (void)threads; (void)grid; (void)cache;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  const int N = base.N;
+
+  // 1. statistics
+  {
+    BwdParams p = base;
+    p.BH = (int)(B * H);
+    void (*kern)(BwdParams) = &fa::fa_bwd_prep_kernel<D>;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)(p.BH * p.T)), dim3(256),
+                                   args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  // 2. dK, dV: one workgroup per 32*KV_NW keys of a K/V head
+  {
+    BwdParams p = base;
+    constexpr int BK = 32 * C::KV_NW;
+    p.BH = (int)(B * H_kv);
+    p.nrb = (N + BK - 1) / BK;
+    p.G = 1;
+    p.xcd_heads = p.BH % 8 == 0 ? 1 : 0;
+    void (*kern)(BwdParams) = &fa::fa_bwd_dkdv_kernel<D, C::KV_NW, C::KV_WPE, CAUSAL>;
+    const int grid = p.nrb * p.BH;
+    static std::atomic<int> cache[kMaxDevices];
+    set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * C::KV_NW, grid, cache);
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * C::KV_NW), args, 0,
+                                   stream);
+    if (e != hipSuccess) return e;
+  }
+  // 3. dQ: one workgroup per 32*Q_NW queries of a query head
+  {
+    BwdParams p = base;
+    constexpr int BR = 32 * C::Q_NW;
+    p.BH = (int)(B * H);
+    p.nrb = (N + BR - 1) / BR;
+    p.G = base.qg;
+    p.xcd_heads = (p.BH / p.G) % 8 == 0 ? 1 : 0;
+    void (*kern)(BwdParams) = &fa::fa_bwd_dq_kernel<D, C::Q_BC, C::Q_NW, C::Q_WPE, CAUSAL>;
+    const int grid = p.nrb * p.BH;
+    static std::atomic<int> cache[kMaxDevices];
+    set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * C::Q_NW, grid, cache);
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * C::Q_NW), args, 0, stream);
+  }
+}
+
+fa_status check_bwd_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int dtype) {
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+  if (B > INT_MAX / H) return FA_ERR_SHAPE;                    // B*H fits an int
+  if (N > (int64_t)INT_MAX / (2 * d)) return FA_ERR_SHAPE;     // one head's bytes fit an int
+  const int64_t bh = B * H;
+  if (bh > INT64_MAX / (N * d * 4)) return FA_ERR_SHAPE;       // byte sizes fit int64
+  // grids: statistics tiles, key blocks and query blocks (at least 64 rows each)
+  if (bh * stat_tiles(N) > INT_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t* bytes) {
+  if (!bytes) return FA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1 || B > INT_MAX / H) return FA_ERR_SHAPE;
+  *bytes = B * H * stat_tiles(N) * (2 * fa::kStatRows) * (int64_t)sizeof(float);
+  return FA_OK;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* workspace, float* dq, float* dk, float* dv, int64_t B, int64_t H, int64_t H_kv, int64_t N,
+                 int64_t d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !workspace || !dq || !dk || !dv) return FA_ERR_NULL;
+  const fa_status st = check_bwd_shape(B, H, H_kv, N, d, dtype);
+  if (st != FA_OK) return st;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)lse, (const void*)workspace, (const void*)dq,
+                          (const void*)dk, (const void*)dv})
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const float c2 = scale * 1.4426950408889634f;
+  if (!std::isfinite(scale) || !std::isfinite(c2)) return FA_ERR_SCALE;
+
+  BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+  p.ws = static_cast<float*>(workspace);
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  p.N = (int)N;
+  p.qg = (int)(H / H_kv);
+  p.T = (int)stat_tiles(N);
+  p.c2 = c2;
+  p.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d == 64) e = causal ? launch_bwd<64, true>(p, B, H, H_kv, s) : launch_bwd<64, false>(p, B, H, H_kv, s);
+  else e = causal ? launch_bwd<128, true>(p, B, H, H_kv, s) : launch_bwd<128, false>(p, B, H, H_kv, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

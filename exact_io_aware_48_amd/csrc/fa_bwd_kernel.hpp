@@ -1,0 +1,450 @@
+// FlashAttention backward for gfx950 (CDNA4): gradients by recomputation.
+//
+// What it computes (per batch b, query head h, K/V head g = h / G): for the
+// loss sum(dO * O) of the forward O = softmax(scale * Q K^T) V,
+//     P  = exp(scale * Q K^T - L)          (L: the forward's per-row logsumexp)
+//     dV = P^T dO                          (summed over the G query heads of g)
+//     dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D)
+//     dQ = scale * dS K,  dK = scale * dS^T Q   (dK summed like dV)
+// The robocikowo.com "Flash Attention" page says the backward pass does not
+// store the N x N matrix but rebuilds it from O and L; the formulas above are
+// the chain rule of the forward definition (systems-analysis.info
+// "FlashAttention (PL)", "Problematyka standardowego mechanizmu uwagi").
+//
+// How (three launches, no atomics, bitwise reproducible):
+//   1. prep:  D = rowsum(dO * O) and L2 = L * log2(e) per query, written to a
+//      caller workspace in 64-query tiles [L2 x 64][D x 64]; rows past N get
+//      L2 = +inf and D = 0, so their P is exactly 0 downstream.
+//   2. dK/dV: a workgroup owns 32*NW keys of one K/V head; each wave keeps its
+//      32 keys' K and V rows in VGPRs (MFMA B operands) and its dK^T, dV^T
+//      accumulators in VGPRs, and streams the Q and dO tiles of all G query
+//      heads through a double-buffered LDS ring.  Per 32-query block:
+//        S = Q K^T and dP = dO V^T  (lane = key, elements over queries),
+//        P and dS in fp32, packed to bf16 straight from the accumulators,
+//        dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read by the LDS
+//        transpose loads (ds_read_b64_tr_b16).
+//      Under the causal mask the query tiles before the key block are never
+//      loaded; key blocks are dispatched earliest (heaviest) first.
+//   3. dQ: a workgroup owns 32*NW queries; each wave keeps Q and dO in
+//      VGPRs and streams K and V tiles, as the forward does:
+//        S^T = K Q^T and dP^T = V dO^T (lane = query),
+//        dQ^T += K^T dS^T with K^T read by the transpose loads.
+//   Tiles that are read both row-wise (ds_read_b128) and transposed share one
+//   XOR swizzle of the 16-byte chunk index that keeps both access patterns
+//   free of LDS bank conflicts (swz_u below).
+//
+// Inputs are bf16; the three gradients are written as fp32.
+#pragma once
+
+#include "fa_common.hpp"
+
+namespace fa {
+
+struct BwdParams {
+  const void* q;       // bf16 [B][H][N][D]
+  const void* k;       // bf16 [B][H_kv][N][D]
+  const void* v;
+  const void* o;       // bf16 [B][H][N][D] (the forward's output)
+  const void* dout;    // bf16 [B][H][N][D]
+  const float* lse;    // [B][H][N], natural log
+  float* ws;           // [B*H][T][2][64]: L2 then D per 64-query tile
+  float* dq;           // fp32 [B][H][N][D]
+  float* dk;           // fp32 [B][H_kv][N][D]
+  float* dv;
+  int BH;              // heads of this launch's grid (B*H for prep and dQ, B*H_kv for dK/dV)
+  int N;
+  int nrb;             // row blocks per head in this launch's grid
+  int G;               // grid mapping: query heads grouped per XCD (dQ: H/H_kv; dK/dV: 1)
+  int qg;              // query heads per K/V head
+  int xcd_heads;
+  int cus_per_xcd;
+  int zigzag;
+  int T;               // 64-query statistics tiles per head (ceil(N / 64))
+  float c2;            // scale * log2(e), signed
+  float scale;
+};
+
+constexpr int kStatRows = 64;   // queries per statistics tile
+
+// Chunk swizzle for tiles read both row-wise (16 lanes x 16 rows at one
+// logical chunk, ds_read_b128) and transposed (32 lanes x 4 rows x 4 adjacent
+// chunks, ds_read_b64_tr_b16).  With RPP rows per 256-byte bank span and
+// rr = row / RPP, the chunk is XORed with 4 * (rr % (CPR/4)) + (rr / (CPR/4)) % 4:
+// the low field differs across any 4 consecutive rows of one bank phase (no
+// two transposed rows collide in a group of 4 chunks) and the whole value
+// is a bijection on 16 consecutive rows of one phase (row reads collide never).
+template <int CPR>
+__device__ __forceinline__ int swz_u(int row) {
+  static_assert(CPR == 8 || CPR == 16, "tile rows of 128 or 256 bytes");
+  constexpr int RPP = CPR >= 16 ? 1 : 16 / CPR;
+  constexpr int A = CPR / 4;
+  const int rr = row / RPP;
+  return 4 * (rr % A) + (rr / A) % 4;
+}
+
+// Per-lane geometry of the operand reads (lane = 32*hf + n).
+struct BwdLane {
+  int n, hf;
+  int t_row, t_col;   // transpose reads: row within a 16-row step, byte column within a 64-byte block
+};
+__device__ __forceinline__ BwdLane bwd_lane(int lane) {
+  BwdLane ln;
+  ln.n = lane & 31;
+  ln.hf = lane >> 5;
+  ln.t_row = 4 * ln.hf + ((lane >> 2) & 3);
+  ln.t_col = 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  return ln;
+}
+
+// A operand rows 32*blk + n of a swizzled bf16 tile, d-step c (dims 16c + 8hf .. +7).
+template <int D>
+__device__ __forceinline__ bf16x8 row_operand(const char FA_LDS* base, int blk, int c, const BwdLane& ln) {
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16;
+  const int row = 32 * blk + ln.n;
+  return __builtin_bit_cast(bf16x8, lds_read16(base + row * ROWB + (((2 * c + ln.hf) ^ swz_u<CPR>(row)) << 4)));
+}
+// A operand X^T (dims 32*db .. +31 as rows) over tile rows
+// 16*s + 8*(i/4) + 4*hf + i%4 of a swizzled bf16 tile (transpose reads).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char FA_LDS* base, int s, int db, const BwdLane& ln) {
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16;
+  const int row = 16 * s + ln.t_row;
+  const int col = 64 * db + ln.t_col;   // bytes
+  const int off0 = row * ROWB + ((((col >> 4) ^ swz_u<CPR>(row)) << 4) | (col & 15));
+  const int off1 = (row + 8) * ROWB + ((((col >> 4) ^ swz_u<CPR>(row + 8)) << 4) | (col & 15));
+  const i16x4 lo = lds_tr16(base + off0), hi = lds_tr16(base + off1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 32 rows x D of a bf16 head (row r0 + n; zeros past N) as MFMA B operand
+// fragments: step c holds dims 16c + 8hf .. +7.
+template <int D>
+__device__ __forceinline__ void load_frag(const void* base, int64_t head_off, int row, int N, const BwdLane& ln,
+                                          bf16x8 (&f)[D / 16]) {
+  const bool ok = row < N;
+  const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(base) + head_off + (int64_t)row * D);
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) f[c] = __builtin_bit_cast(bf16x8, ok ? src[2 * c + ln.hf] : i32x4{0, 0, 0, 0});
+}
+
+// HBM -> LDS staging of a ROWS x D bf16 tile with the swz_u swizzle, by all NW
+// waves.  Rows past N re-read row N-1 (their contributions are zeroed by the
+// caller's statistics or mask).
+template <int D, int ROWS, int NW>
+struct UStager {
+  static constexpr int ROWB = 2 * D, CPR = ROWB / 16;
+  static constexpr int UNITS = ROWS * ROWB / 16;
+  static constexpr int UPT = UNITS / (NW * 64);
+  static_assert(UNITS % (NW * 64) == 0, "tile splits evenly over the waves");
+  int ofs[UPT];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int off = (i * NW + wave) * 1024 + lane * 16;
+      const int row = off / ROWB, pc = (off % ROWB) >> 4;
+      ofs[i] = row * ROWB + ((pc ^ swz_u<CPR>(row)) << 4);
+    }
+  }
+  // rows row0 .. row0+ROWS-1 of the head at glob (bytes) -> LDS at dst
+  __device__ __forceinline__ void issue(const char* glob, int row0, int N, char FA_LDS* dst, int wave, int lane) const {
+    const char* base = glob + (int64_t)row0 * ROWB;
+    if (row0 + ROWS <= N) {
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) dma16_s(base, ofs[i], dst + (i * NW + wave) * 1024);
+    } else {
+      const int last = N - 1 - row0;
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) {
+        const int off = (i * NW + wave) * 1024 + lane * 16;
+        const int row = off / ROWB, pc = (off % ROWB) >> 4;
+        dma16_s(base, min(row, last) * ROWB + ((pc ^ swz_u<CPR>(row)) << 4), dst + (i * NW + wave) * 1024);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- 1. prep
+// One workgroup of 256 threads per 64-query tile of one head; D / 8 threads
+// share a row, each summing 8 products in fp32.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;          // threads per row
+  constexpr int RPI = 256 / TPR;      // rows per pass
+  const int bh = blockIdx.x / p.T, t = blockIdx.x - bh * p.T;
+  const int r = threadIdx.x / TPR, c = threadIdx.x % TPR;
+  const int64_t head = (int64_t)bh * p.N * D;
+  float* out = p.ws + ((int64_t)bh * p.T + t) * (2 * kStatRows);
+#pragma unroll
+  for (int it = 0; it < kStatRows / RPI; ++it) {
+    const int row = it * RPI + r, qi = t * kStatRows + row;
+    float acc = 0.f;
+    if (qi < p.N) {
+      const i32x4 a = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.o) + head + (int64_t)qi * D + 8 * c);
+      const i32x4 b = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.dout) + head + (int64_t)qi * D + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_fmaf(bf16_lo_to_f32(a[j]), bf16_lo_to_f32(b[j]), acc);
+        acc = __builtin_fmaf(bf16_hi_to_f32(a[j]), bf16_hi_to_f32(b[j]), acc);
+      }
+    }
+#pragma unroll
+    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (c == 0) {
+      out[row] = qi < p.N ? p.lse[(int64_t)bh * p.N + qi] * kLog2e : INFINITY;
+      out[kStatRows + row] = qi < p.N ? acc : 0.f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 2. dK / dV
+template <int D, int NW, int WPE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void fa_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BQ = kStatRows;             // queries per tile
+  constexpr int BK = 32 * NW;               // keys per workgroup
+  constexpr int ROWB = 2 * D;
+  constexpr int TILEB = BQ * ROWB;
+  constexpr int STATB = 1024;               // L2 and D of the tile (512 B), then a copy
+  constexpr int STAGEB = 2 * TILEB + STATB;
+  constexpr int NSTEP = D / 16, NDB = D / 32;
+  static_assert(2 * STAGEB <= 160 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB];
+  char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const BwdLane ln = bwd_lane(lane);
+
+  int bhk, rb;
+  map_block<CAUSAL>(p, blockIdx.x, bhk, rb);
+  const int kb = p.nrb - 1 - rb;            // causal: earliest key blocks (most query tiles) first
+  const int N = p.N;
+  const int k0 = kb * BK, kw0 = k0 + 32 * wave, my_key = kw0 + ln.n;
+  const int64_t kv_off = (int64_t)bhk * N * D;
+
+  bf16x8 kf[NSTEP], vf[NSTEP];
+  load_frag<D>(p.k, kv_off, my_key, N, ln, kf);
+  load_frag<D>(p.v, kv_off, my_key, N, ln, vf);
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) dk[b] = dv[b] = f32x16{};
+
+  const int T = p.T;
+  const int t0 = CAUSAL ? k0 / BQ : 0;      // earlier query tiles see none of these keys
+  const int nt = T - t0;
+  const int n_iter = p.qg * nt;             // (query head, query tile) pairs
+
+  UStager<D, BQ, NW> stage;
+  stage.init(wave, lane);
+  auto issue = [&](int it, char FA_LDS* dst) __attribute__((always_inline)) {
+    const int hh = it / nt, t = t0 + it - hh * nt;
+    const int64_t bhq = (int64_t)bhk * p.qg + hh;
+    const char* qglob = static_cast<const char*>(p.q) + bhq * N * ROWB;
+    const char* oglob = static_cast<const char*>(p.dout) + bhq * N * ROWB;
+    stage.issue(qglob, t * BQ, N, dst, wave, lane);
+    stage.issue(oglob, t * BQ, N, dst + TILEB, wave, lane);
+    if (wave == 0) {
+      const float* src = p.ws + (bhq * T + t) * (2 * kStatRows) + 4 * (lane & 31);
+      dma16(src, dst + 2 * TILEB);
+    }
+  };
+
+  const float c2 = p.c2;
+  auto tile = [&](int it, const char FA_LDS* qs) __attribute__((always_inline)) {
+    const int hh = it / nt, t = t0 + it - hh * nt;
+    (void)hh;
+    const int qt0 = t * BQ;
+    if (CAUSAL && qt0 + BQ - 1 < kw0) return;          // every query of the tile precedes every key of the wave
+    const char FA_LDS* dos = qs + TILEB;
+    const char FA_LDS* st = qs + 2 * TILEB;
+    const bool diag = CAUSAL && qt0 < kw0 + 31;
+    const int lim = kw0 + ln.n - qt0 - 4 * ln.hf;       // keep element iff its query offset >= lim
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      f32x16 s{}, dp{};
+#pragma unroll
+      for (int c = 0; c < NSTEP; ++c) {
+        s = mfma_bf16(row_operand<D>(qs, qb, c, ln), kf[c], s);
+        dp = mfma_bf16(row_operand<D>(dos, qb, c, ln), vf[c], dp);
+      }
+      float pr[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qo = 32 * qb + 8 * g + 4 * ln.hf;     // query offset of elements 4g .. 4g+3
+        const f32x4 l2 = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * qo);
+        const f32x4 dd = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * (kStatRows + qo));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2[e]));
+          if (diag) x = (32 * qb + 8 * g + e) >= lim ? x : 0.f;
+          pr[i] = x;
+          ds[i] = x * (dp[i] - dd[e]);
+        }
+      }
+      // B operands of the two 16-query steps of this block (element i' of step
+      // u <- accumulator element 8u + i')
+      i32x4 pp[2], dsp[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pp[u][w] = (int)pack_bf16x2(pr[8 * u + 2 * w], pr[8 * u + 2 * w + 1]);
+          dsp[u][w] = (int)pack_bf16x2(ds[8 * u + 2 * w], ds[8 * u + 2 * w + 1]);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          dv[db] = mfma_bf16(tr_operand<D>(dos, 2 * qb + u, db, ln), __builtin_bit_cast(bf16x8, pp[u]), dv[db]);
+          dk[db] = mfma_bf16(tr_operand<D>(qs, 2 * qb + u, db, ln), __builtin_bit_cast(bf16x8, dsp[u]), dk[db]);
+        }
+    }
+  };
+
+  auto slot = [&](int s) __attribute__((always_inline)) { return smem + s * STAGEB; };
+  if (n_iter > 0) {
+    issue(0, slot(0));
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int it = 0; it < n_iter; ++it) {
+    if (it + 1 < n_iter) issue(it + 1, slot(cur ^ 1));
+    tile(it, slot(cur));
+    wait_vmcnt<0>();
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  if (my_key < N) {
+    float* dkp = p.dk + kv_off + (int64_t)my_key * D;
+    float* dvp = p.dv + kv_off + (int64_t)my_key * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * ln.hf;
+        *reinterpret_cast<f32x4*>(dkp + col) =
+            f32x4{dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc};
+        *reinterpret_cast<f32x4*>(dvp + col) = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- 3. dQ
+template <int D, int BC, int NW, int WPE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int BR = 32 * NW;
+  constexpr int ROWB = 2 * D;
+  constexpr int TILEB = BC * ROWB;
+  constexpr int STAGEB = 2 * TILEB;          // K tile, V tile
+  constexpr int NSTEP = D / 16, NDB = D / 32, KB = BC / 32;
+  static_assert(2 * STAGEB <= 160 * 1024, "LDS budget");
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB];
+  char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const BwdLane ln = bwd_lane(lane);
+
+  int bh, rb;
+  map_block<CAUSAL>(p, blockIdx.x, bh, rb);
+  const int N = p.N;
+  const int q_row0 = rb * BR, qw0 = q_row0 + 32 * wave, my_q = qw0 + ln.n;
+  const int64_t head_off = (int64_t)bh * N * D;
+  const int64_t kv_off = (int64_t)(bh / p.qg) * N * D;
+
+  bf16x8 qf[NSTEP], of[NSTEP];
+  load_frag<D>(p.q, head_off, my_q, N, ln, qf);
+  load_frag<D>(p.dout, head_off, my_q, N, ln, of);
+  float l2 = INFINITY, dd = 0.f;              // queries past the padded tiles: P = 0
+  if (my_q < p.T * kStatRows) {
+    const float* w = p.ws + ((int64_t)bh * p.T + my_q / kStatRows) * (2 * kStatRows) + my_q % kStatRows;
+    l2 = w[0];
+    dd = w[kStatRows];
+  }
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) dq[b] = f32x16{};
+
+  const int tiles_all = (N + BC - 1) / BC;
+  const int n_tiles = CAUSAL ? min(tiles_all, (q_row0 + BR - 1) / BC + 1) : tiles_all;
+  const int wave_tiles = CAUSAL ? min(tiles_all, (qw0 + 31) / BC + 1) : tiles_all;
+  const int last_key = (CAUSAL ? min(N - 1, my_q) : N - 1) - 4 * ln.hf;
+
+  UStager<D, BC, NW> stage;
+  stage.init(wave, lane);
+  const char* kglob = static_cast<const char*>(p.k) + kv_off * 2;
+  const char* vglob = static_cast<const char*>(p.v) + kv_off * 2;
+  auto slot = [&](int s) __attribute__((always_inline)) { return smem + s * STAGEB; };
+  auto issue = [&](int j, char FA_LDS* dst) __attribute__((always_inline)) {
+    stage.issue(kglob, j * BC, N, dst, wave, lane);
+    stage.issue(vglob, j * BC, N, dst + TILEB, wave, lane);
+  };
+
+  const float c2 = p.c2;
+  auto tile = [&](int j, const char FA_LDS* ks) __attribute__((always_inline)) {
+    const char FA_LDS* vs = ks + TILEB;
+    const int key0 = j * BC;
+    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0);
+    const int lim = last_key - key0;
+    i32x4 dsp[2 * KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 s{}, dp{};
+#pragma unroll
+      for (int c = 0; c < NSTEP; ++c) {
+        s = mfma_bf16(row_operand<D>(ks, kb, c, ln), qf[c], s);
+        dp = mfma_bf16(row_operand<D>(vs, kb, c, ln), of[c], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2));
+        if (need_mask) x = (32 * kb + 8 * (i >> 2) + (i & 3)) > lim ? 0.f : x;
+        ds[i] = x * (dp[i] - dd);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dsp[2 * kb + u][w] = (int)pack_bf16x2(ds[8 * u + 2 * w], ds[8 * u + 2 * w + 1]);
+    }
+#pragma unroll
+    for (int s = 0; s < 2 * KB; ++s)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dq[db] = mfma_bf16(tr_operand<D>(ks, s, db, ln), __builtin_bit_cast(bf16x8, dsp[s]), dq[db]);
+  };
+
+  issue(0, slot(0));
+  wait_vmcnt<0>();
+  __syncthreads();
+  int cur = 0;
+  for (int j = 0; j < n_tiles; ++j) {
+    if (j + 1 < n_tiles) issue(j + 1, slot(cur ^ 1));
+    if (j < wave_tiles) tile(j, slot(cur));
+    wait_vmcnt<0>();
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  if (my_q < N) {
+    float* dst = p.dq + head_off + (int64_t)my_q * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * db + 8 * g + 4 * ln.hf;
+        *reinterpret_cast<f32x4*>(dst + col) =
+            f32x4{dq[db][4 * g] * sc, dq[db][4 * g + 1] * sc, dq[db][4 * g + 2] * sc, dq[db][4 * g + 3] * sc};
+      }
+  }
+}
+
+}  // namespace fa

@@ -187,11 +187,13 @@ __device__ __forceinline__ int zigzag_slot(int s, int total, int C) {
   const int R = min(C, total - base);          // slots in this round
   return base + ((r & 1) ? R - 1 - pos : pos);
 }
-__device__ __forceinline__ int xcd_head(const Params& p, int xcd, int hl) {
+// P: any parameter block with the fields BH, nrb, G, xcd_heads, zigzag and cus_per_xcd.
+template <class P>
+__device__ __forceinline__ int xcd_head(const P& p, int xcd, int hl) {
   return p.G * (xcd + 8 * (hl / p.G)) + hl % p.G;
 }
-template <bool CAUSAL>
-__device__ __forceinline__ void map_block(const Params& p, int id, int& bh, int& rb) {
+template <bool CAUSAL, class P>
+__device__ __forceinline__ void map_block(const P& p, int id, int& bh, int& rb) {
   const int nrb = p.nrb;
   if constexpr (!CAUSAL) {
     if (p.xcd_heads) {

@@ -9,7 +9,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fa_fwd.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,14 +23,16 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_plan",
-                                    "fa_status_string", "fa_version"]
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa",
+                                    "fa_fwd_gqa_fp8", "fa_plan", "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -116,3 +119,33 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libfa_fwd.so")
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_fa_bwd_workspace_size(lib):
+    n = ctypes.c_int64()
+    assert lib.fa_bwd_workspace_size(2, 3, 100, ctypes.byref(n)) == 0 and n.value == 2 * 3 * 2 * 128 * 4
+    assert lib.fa_bwd_workspace_size(1, 1, 64, ctypes.byref(n)) == 0 and n.value == 512
+    assert lib.fa_bwd_workspace_size(1, 1, 65, ctypes.byref(n)) == 0 and n.value == 1024
+    assert lib.fa_bwd_workspace_size(1, 1, 64, None) == 1
+    assert lib.fa_bwd_workspace_size(0, 1, 64, ctypes.byref(n)) == 2
+    assert lib.fa_bwd_workspace_size(1, 1, 0, ctypes.byref(n)) == 2
+
+
+def _bwd_args(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, ws=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=1, H=2, H_kv=2, N=64, d=64, scale=0.1, causal=0, dtype=1)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "o", "do", "lse", "ws", "dq", "dk", "dv", "B", "H", "H_kv", "N", "d",
+                           "scale", "causal", "dtype")] + [None]
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"q": 0}, 1), ({"do": 0}, 1), ({"lse": 0}, 1), ({"ws": 0}, 1), ({"dv": 0}, 1),
+    ({"B": 0}, 2), ({"N": 0}, 2), ({"H_kv": 0}, 2), ({"H_kv": 3}, 2), ({"H": 2, "H_kv": 4}, 2),
+    ({"N": 2**40}, 2), ({"B": 2**31, "H": 2**31}, 2),
+    ({"d": 256}, 3), ({"d": 96}, 3), ({"dtype": 0}, 3), ({"dtype": 2}, 3),
+    ({"o": FAKE + 8}, 4), ({"ws": FAKE + 4}, 4), ({"dk": FAKE + 2}, 4),
+    ({"scale": float("inf")}, 5), ({"scale": float("nan")}, 5), ({"scale": 3e38}, 5),
+])
+def test_fa_bwd_validation(lib, kw, expected):
+    assert lib.fa_bwd(*_bwd_args(**kw)) == expected
