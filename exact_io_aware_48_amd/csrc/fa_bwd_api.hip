@@ -9,6 +9,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "fa_bwd.h"
 #include "fa_bwd_kernel.hpp"
@@ -18,16 +19,27 @@ namespace {
 
 using fa::BwdParams;
 
-// Shapes per head dim.  dK/dV: NW waves of 32 keys, each holding K, V and
-// the two fp32 accumulators in VGPRs (d = 128 needs more than 256 VGPRs, so
-// one wave per SIMD).  dQ: NW waves of 32 queries, B_c-key K/V tiles.
+// Shapes per head dim.  dK/dV: NW waves of 32 keys, each holding K and the
+// two fp32 accumulators in VGPRs.  At d = 128 the main shape stages V in LDS
+// (K, V and the accumulators would not fit the 256 VGPRs of two waves per
+// SIMD) and gives a workgroup 256 keys; a causal grid of those that fills
+// fewer than two rounds of resident workgroups is dominated by its heaviest
+// (earliest) key blocks, so it takes the small shape instead: 128 keys, one
+// wave per SIMD with K and V in VGPRs.  At d = 64 V stays in VGPRs.
+// dQ: NW waves of 32 queries, B_c-key K/V tiles.
+template <int NW_, int WPE_, bool VLDS_> struct KvShape {
+  static constexpr int NW = NW_, WPE = WPE_;
+  static constexpr bool VLDS = VLDS_;
+};
 template <int D> struct BwdCfg;
 template <> struct BwdCfg<64> {
-  static constexpr int KV_NW = 4, KV_WPE = 2;
+  using KV = KvShape<4, 2, false>;
+  using KV_SMALL = KV;
   static constexpr int Q_BC = 64, Q_NW = 4, Q_WPE = 2;
 };
 template <> struct BwdCfg<128> {
-  static constexpr int KV_NW = 4, KV_WPE = 1;
+  using KV = KvShape<8, 2, true>;
+  using KV_SMALL = KvShape<4, 1, false>;
   static constexpr int Q_BC = 64, Q_NW = 8, Q_WPE = 2;
 };
 
@@ -46,6 +58,37 @@ void set_balance(BwdParams& p, const void* kern, int threads, int grid, std::ato
   }
 }
 
+template <int D, bool CAUSAL, class S>
+hipError_t launch_dkdv_shape(const BwdParams& base, int64_t BHkv, hipStream_t stream) {
+  BwdParams p = base;
+  constexpr int BK = 32 * S::NW;
+  p.BH = (int)BHkv;
+  p.nrb = (base.N + BK - 1) / BK;
+  p.G = 1;
+  p.xcd_heads = p.BH % 8 == 0 ? 1 : 0;
+  void (*kern)(BwdParams) = &fa::fa_bwd_dkdv_kernel<D, S::NW, S::WPE, CAUSAL, S::VLDS>;
+  const int grid = p.nrb * p.BH;
+  static std::atomic<int> cache[kMaxDevices];
+  set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * S::NW, grid, cache);
+  void* args[] = {&p};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * S::NW), args, 0, stream);
+}
+
+template <int D, bool CAUSAL, class BIG, class SMALL>
+hipError_t launch_dkdv(const BwdParams& base, int64_t BHkv, hipStream_t stream) {
+  if constexpr (CAUSAL && !std::is_same<BIG, SMALL>::value) {
+    constexpr int BK = 32 * BIG::NW;
+    static std::atomic<int> cache[kMaxDevices];
+    const Residency r = residency(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, BIG::NW, BIG::WPE, CAUSAL,
+                                                                                        BIG::VLDS>),
+                                  64 * BIG::NW, cache);
+    const int64_t grid = (base.N + BK - 1) / BK * BHkv;
+    if (r.resident > 0 && grid < 2 * (int64_t)r.resident)
+      return launch_dkdv_shape<D, CAUSAL, SMALL>(base, BHkv, stream);
+  }
+  return launch_dkdv_shape<D, CAUSAL, BIG>(base, BHkv, stream);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv, hipStream_t stream) {
   using C = BwdCfg<D>;
@@ -61,21 +104,9 @@ hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv,
                                    args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  // 2. dK, dV: one workgroup per 32*KV_NW keys of a K/V head
+  // 2. dK, dV: one workgroup per 32*NW keys of a K/V head
   {
-    BwdParams p = base;
-    constexpr int BK = 32 * C::KV_NW;
-    p.BH = (int)(B * H_kv);
-    p.nrb = (N + BK - 1) / BK;
-    p.G = 1;
-    p.xcd_heads = p.BH % 8 == 0 ? 1 : 0;
-    void (*kern)(BwdParams) = &fa::fa_bwd_dkdv_kernel<D, C::KV_NW, C::KV_WPE, CAUSAL>;
-    const int grid = p.nrb * p.BH;
-    static std::atomic<int> cache[kMaxDevices];
-    set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * C::KV_NW, grid, cache);
-    void* args[] = {&p};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * C::KV_NW), args, 0,
-                                   stream);
+    hipError_t e = launch_dkdv<D, CAUSAL, typename C::KV, typename C::KV_SMALL>(base, B * H_kv, stream);
     if (e != hipSuccess) return e;
   }
   // 3. dQ: one workgroup per 32*Q_NW queries of a query head

@@ -197,56 +197,141 @@ __global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- 2. dK / dV
-template <int D, int NW, int WPE, bool CAUSAL>
+// v_mfma_f32_16x16x32_bf16 on a wave64, lane = 16*g + m:
+//   A (16 x 32): lane holds row m, k-slots 8g .. 8g+7
+//   B (32 x 16): lane holds column m, the same k-slots
+//   C (16 x 16): lane holds column m, rows 4g .. 4g+3
+// S and dP are 16-query x 16-key blocks with the key in the lane (column)
+// and the queries along the elements, so P and dS feed dV^T += dO^T P and
+// dK^T += Q^T dS as B operands straight from the accumulators: k-slot
+// (g, i) of a 32-query step is query 16*(i/4) + 4g + i%4 of that step, and
+// the matching dO^T / Q^T operand is two transpose reads of rows 4g .. 4g+3
+// and 16 + 4g .. 16 + 4g+3.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Chunk swizzle of the tiles the dK/dV kernel reads row-wise (16 rows at one
+// logical chunk) and transposed (8 consecutive rows x 2 adjacent chunks per
+// 32 lanes): with rr = row / RPP, XOR with 2 * (rr % (CPR/2)) + (rr / (CPR/2)) % 2,
+// a bijection on 16 consecutive rows of one bank phase whose upper bits
+// differ across 8 consecutive rows (4 per phase when two rows share a span).
+template <int CPR>
+__device__ __forceinline__ int swz16(int row) {
+  static_assert(CPR == 8 || CPR == 16, "tile rows of 128 or 256 bytes");
+  constexpr int RPP = CPR >= 16 ? 1 : 16 / CPR;
+  constexpr int A = CPR / 2;
+  const int rr = row / RPP;
+  return 2 * (rr % A) + (rr / A) % 2;
+}
+
+// HBM -> LDS staging of ROWS x D bf16 rows with swz16, by all NW waves
+// (rows past N re-read row N-1).
+template <int D, int ROWS, int NW>
+struct Stager16 {
+  static constexpr int ROWB = 2 * D, CPR = ROWB / 16;
+  static constexpr int UNITS = ROWS * ROWB / 16;
+  static constexpr int UPT = UNITS / (NW * 64);
+  static_assert(UNITS % (NW * 64) == 0, "tile splits evenly over the waves");
+  __device__ __forceinline__ void issue(const char* glob, int row0, int N, char FA_LDS* dst, int wave, int lane) const {
+    const char* base = glob + (int64_t)row0 * ROWB;
+    const int last = N - 1 - row0;
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int off = (i * NW + wave) * 1024 + lane * 16;
+      const int row = off / ROWB, pc = (off % ROWB) >> 4;
+      dma16_s(base, min(row, last) * ROWB + ((pc ^ swz16<CPR>(row)) << 4), dst + (i * NW + wave) * 1024);
+    }
+  }
+};
+
+// A workgroup owns BK = 32*NW keys of one K/V head; wave w owns keys
+// 32w .. 32w+31 as two 16-key blocks.  K stays in VGPRs as B operands; V
+// (VLDS) is staged once into LDS and read as B operands, or kept in VGPRs.
+template <int D, int NW, int WPE, bool CAUSAL, bool VLDS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int BQ = kStatRows;             // queries per tile
   constexpr int BK = 32 * NW;               // keys per workgroup
-  constexpr int ROWB = 2 * D;
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16;
   constexpr int TILEB = BQ * ROWB;
   constexpr int STATB = 1024;               // L2 and D of the tile (512 B), then a copy
   constexpr int STAGEB = 2 * TILEB + STATB;
-  constexpr int NSTEP = D / 16, NDB = D / 32;
-  static_assert(2 * STAGEB <= 160 * 1024, "LDS budget");
+  constexpr int VBYTES = VLDS ? BK * ROWB : 0;
+  constexpr int NC = D / 32;                // 32-dim k-steps of S and dP
+  constexpr int NDB = D / 16;               // 16-dim blocks of dK^T and dV^T
+  static_assert(2 * STAGEB + VBYTES <= 160 * 1024, "LDS budget");
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB];
+  __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB + (VLDS ? VBYTES : 16)];
   char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
+  char FA_LDS* const vsm = smem + 2 * STAGEB;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const BwdLane ln = bwd_lane(lane);
+  const int m = lane & 15, g = lane >> 4;
 
   int bhk, rb;
   map_block<CAUSAL>(p, blockIdx.x, bhk, rb);
-  const int kb = p.nrb - 1 - rb;            // causal: earliest key blocks (most query tiles) first
+  const int kblk = p.nrb - 1 - rb;          // causal: earliest key blocks (most query tiles) first
   const int N = p.N;
-  const int k0 = kb * BK, kw0 = k0 + 32 * wave, my_key = kw0 + ln.n;
+  const int k0 = kblk * BK, kw0 = k0 + 32 * wave;
   const int64_t kv_off = (int64_t)bhk * N * D;
 
-  bf16x8 kf[NSTEP], vf[NSTEP];
-  load_frag<D>(p.k, kv_off, my_key, N, ln, kf);
-  load_frag<D>(p.v, kv_off, my_key, N, ln, vf);
-
-  f32x16 dk[NDB], dv[NDB];
+  // K (and V) rows kw0 + 16*kb + m: chunk 4c + g of each row (zeros past N)
+  bf16x8 kf[2][NC], vf[2][VLDS ? 1 : NC];
 #pragma unroll
-  for (int b = 0; b < NDB; ++b) dk[b] = dv[b] = f32x16{};
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw0 + 16 * kb + m;
+    const bool ok = key < N;
+    const i32x4* ks = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.k) + kv_off + (int64_t)key * D);
+    const i32x4* vs = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.v) + kv_off + (int64_t)key * D);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      kf[kb][c] = __builtin_bit_cast(bf16x8, ok ? ks[4 * c + g] : i32x4{0, 0, 0, 0});
+      if constexpr (!VLDS) vf[kb][c] = __builtin_bit_cast(bf16x8, ok ? vs[4 * c + g] : i32x4{0, 0, 0, 0});
+    }
+  }
+
+  f32x4 dk[2][NDB], dv[2][NDB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int b = 0; b < NDB; ++b) dk[kb][b] = dv[kb][b] = f32x4{};
 
   const int T = p.T;
   const int t0 = CAUSAL ? k0 / BQ : 0;      // earlier query tiles see none of these keys
   const int nt = T - t0;
   const int n_iter = p.qg * nt;             // (query head, query tile) pairs
 
-  UStager<D, BQ, NW> stage;
-  stage.init(wave, lane);
+  Stager16<D, BQ, NW> stage;
   auto issue = [&](int it, char FA_LDS* dst) __attribute__((always_inline)) {
     const int hh = it / nt, t = t0 + it - hh * nt;
     const int64_t bhq = (int64_t)bhk * p.qg + hh;
-    const char* qglob = static_cast<const char*>(p.q) + bhq * N * ROWB;
-    const char* oglob = static_cast<const char*>(p.dout) + bhq * N * ROWB;
-    stage.issue(qglob, t * BQ, N, dst, wave, lane);
-    stage.issue(oglob, t * BQ, N, dst + TILEB, wave, lane);
-    if (wave == 0) {
-      const float* src = p.ws + (bhq * T + t) * (2 * kStatRows) + 4 * (lane & 31);
-      dma16(src, dst + 2 * TILEB);
+    stage.issue(static_cast<const char*>(p.q) + bhq * N * ROWB, t * BQ, N, dst, wave, lane);
+    stage.issue(static_cast<const char*>(p.dout) + bhq * N * ROWB, t * BQ, N, dst + TILEB, wave, lane);
+    if (wave == 0) dma16(p.ws + (bhq * T + t) * (2 * kStatRows) + 4 * (lane & 31), dst + 2 * TILEB);
+  };
+
+  // A operand: rows 16*qb + m of a Q or dO tile, dims 32c + 8g .. +7
+  auto row_a = [&](const char FA_LDS* base, int qb, int c) __attribute__((always_inline)) {
+    const int row = 16 * qb + m;
+    return __builtin_bit_cast(bf16x8, lds_read16(base + row * ROWB + (((4 * c + g) ^ swz16<CPR>(row)) << 4)));
+  };
+  // A operand X^T: dims 16*db + m over the queries of 32-query step s in k-slot order
+  auto tr_a = [&](const char FA_LDS* base, int s, int db) __attribute__((always_inline)) {
+    const int row = 32 * s + 4 * g + ((lane >> 2) & 3);
+    const int col = 32 * db + 8 * (lane & 3);   // bytes
+    const int off0 = row * ROWB + ((((col >> 4) ^ swz16<CPR>(row)) << 4) | (col & 15));
+    const int off1 = (row + 16) * ROWB + ((((col >> 4) ^ swz16<CPR>(row + 16)) << 4) | (col & 15));
+    const i16x4 lo = lds_tr16(base + off0), hi = lds_tr16(base + off1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // B operand V^T: keys 32*wave + 16*kb + m, dims 32c + 8g .. +7
+  auto v_b = [&](int kb, int c) __attribute__((always_inline)) {
+    if constexpr (VLDS) {
+      const int row = 32 * wave + 16 * kb + m;
+      return __builtin_bit_cast(bf16x8, lds_read16(vsm + row * ROWB + (((4 * c + g) ^ swz16<CPR>(row)) << 4)));
+    } else {
+      return vf[kb][c];
     }
   };
 
@@ -259,55 +344,69 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const char FA_LDS* dos = qs + TILEB;
     const char FA_LDS* st = qs + 2 * TILEB;
     const bool diag = CAUSAL && qt0 < kw0 + 31;
-    const int lim = kw0 + ln.n - qt0 - 4 * ln.hf;       // keep element iff its query offset >= lim
+    const int lim = kw0 + m - qt0 - 4 * g;              // keep element iff its (query - key) offset >= lim
 #pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      f32x16 s{}, dp{};
+    for (int s = 0; s < BQ / 32; ++s) {
+      i32x4 pp[2], dsp[2];                              // B operands of this 32-query step, per key block
 #pragma unroll
-      for (int c = 0; c < NSTEP; ++c) {
-        s = mfma_bf16(row_operand<D>(qs, qb, c, ln), kf[c], s);
-        dp = mfma_bf16(row_operand<D>(dos, qb, c, ln), vf[c], dp);
-      }
-      float pr[16], ds[16];
+      for (int h = 0; h < 2; ++h) {
+        const int qb = 2 * s + h;
+        f32x4 sc[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qo = 32 * qb + 8 * g + 4 * ln.hf;     // query offset of elements 4g .. 4g+3
-        const f32x4 l2 = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * qo);
-        const f32x4 dd = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * (kStatRows + qo));
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 aq = row_a(qs, qb, c);
+          const bf16x8 ao = row_a(dos, qb, c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2[e]));
-          if (diag) x = (32 * qb + 8 * g + e) >= lim ? x : 0.f;
-          pr[i] = x;
-          ds[i] = x * (dp[i] - dd[e]);
+          for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = mfma16(aq, kf[kb][c], sc[kb]);
+            dp[kb] = mfma16(ao, v_b(kb, c), dp[kb]);
+          }
+        }
+        const f32x4 l2 = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * (16 * qb + 4 * g));
+        const f32x4 dd = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * (kStatRows + 16 * qb + 4 * g));
+        float pr[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pr[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j], c2, -l2[j]));
+        if (diag) {
+          asm volatile("" ::: "memory");                // keep this a branch: only diagonal tiles mask
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[kb][j] = (16 * qb + j - 16 * kb) >= lim ? pr[kb][j] : 0.f;
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float ds[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ds[j] = pr[kb][j] * (dp[kb][j] - dd[j]);
+          pp[kb][2 * h] = (int)pack_bf16x2(pr[kb][0], pr[kb][1]);
+          pp[kb][2 * h + 1] = (int)pack_bf16x2(pr[kb][2], pr[kb][3]);
+          dsp[kb][2 * h] = (int)pack_bf16x2(ds[0], ds[1]);
+          dsp[kb][2 * h + 1] = (int)pack_bf16x2(ds[2], ds[3]);
         }
       }
-      // B operands of the two 16-query steps of this block (element i' of step
-      // u <- accumulator element 8u + i')
-      i32x4 pp[2], dsp[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 ao = tr_a(dos, s, db);
+        const bf16x8 aq = tr_a(qs, s, db);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pp[u][w] = (int)pack_bf16x2(pr[8 * u + 2 * w], pr[8 * u + 2 * w + 1]);
-          dsp[u][w] = (int)pack_bf16x2(ds[8 * u + 2 * w], ds[8 * u + 2 * w + 1]);
+        for (int kb = 0; kb < 2; ++kb) {
+          dv[kb][db] = mfma16(ao, __builtin_bit_cast(bf16x8, pp[kb]), dv[kb][db]);
+          dk[kb][db] = mfma16(aq, __builtin_bit_cast(bf16x8, dsp[kb]), dk[kb][db]);
         }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = mfma_bf16(tr_operand<D>(dos, 2 * qb + u, db, ln), __builtin_bit_cast(bf16x8, pp[u]), dv[db]);
-          dk[db] = mfma_bf16(tr_operand<D>(qs, 2 * qb + u, db, ln), __builtin_bit_cast(bf16x8, dsp[u]), dk[db]);
-        }
+      }
     }
   };
 
   auto slot = [&](int s) __attribute__((always_inline)) { return smem + s * STAGEB; };
-  if (n_iter > 0) {
-    issue(0, slot(0));
-    wait_vmcnt<0>();
+  if constexpr (VLDS) {
+    Stager16<D, BK, NW> vstage;
+    vstage.issue(static_cast<const char*>(p.v) + kv_off * 2, k0, N, vsm, wave, lane);
   }
+  issue(0, slot(0));
+  wait_vmcnt<0>();
   __syncthreads();
   int cur = 0;
   for (int it = 0; it < n_iter; ++it) {
@@ -318,19 +417,19 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     cur ^= 1;
   }
 
-  if (my_key < N) {
-    float* dkp = p.dk + kv_off + (int64_t)my_key * D;
-    float* dvp = p.dv + kv_off + (int64_t)my_key * D;
-    const float sc = p.scale;
+  const float sc = p.scale;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = kw0 + 16 * kb + m;
+    if (key < N) {
+      float* dkp = p.dk + kv_off + (int64_t)key * D + 4 * g;
+      float* dvp = p.dv + kv_off + (int64_t)key * D + 4 * g;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * ln.hf;
-        *reinterpret_cast<f32x4*>(dkp + col) =
-            f32x4{dk[db][4 * g] * sc, dk[db][4 * g + 1] * sc, dk[db][4 * g + 2] * sc, dk[db][4 * g + 3] * sc};
-        *reinterpret_cast<f32x4*>(dvp + col) = f32x4{dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      for (int db = 0; db < NDB; ++db) {
+        *reinterpret_cast<f32x4*>(dkp + 16 * db) = dk[kb][db] * sc;
+        *reinterpret_cast<f32x4*>(dvp + 16 * db) = dv[kb][db];
       }
+    }
   }
 }
 

@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_backward, delta_rows, dkdv_cols, dq_rows
+from oracle import attention_backward, backward_head, delta_rows, dkdv_cols, dq_rows
 from workloads import bf16_bits_from_f32, bf16_bits_to_f64, by_name, make_grad_output, make_inputs
 
 from gpu_util import oracle_full, run_gpu, to_device
@@ -187,6 +187,22 @@ def test_forward_then_backward(B, H, H_kv, N, d, causal):
     do = make_grad_output(w)
     o, l = _fwd_from_gpu(x)
     check_grads(run_bwd(x, do, o, l), oracle_bwd(x, do), f"fwd+bwd B={B} H={H} N={N} d={d}")
+
+
+def test_backward_many_heads_ragged():
+    """Enough K/V heads that the causal dK/dV grid takes the 256-key workgroups
+    (at least two rounds of resident workgroups), with a ragged length;
+    sampled heads compared on every element."""
+    w = _case(1, 64, 64, 2049, 128, True, seed=41)
+    _print_case("many-heads", w.H, w.N)
+    x = make_inputs(w)
+    do = make_grad_output(w)
+    o, l = _fwd_from_gpu(x)
+    dq, dk, dv = run_bwd(x, do, o, l)
+    do64 = bf16_bits_to_f64(do)
+    for h in (0, 31, 63):
+        ref = backward_head(x.f64("q", 0, h), x.f64("k", 0, h), x.f64("v", 0, h), do64[0, h], w.softmax_scale, True)
+        check_grads((dq[0, h], dk[0, h], dv[0, h]), ref, f"many heads, head {h}")
 
 
 # ---------------------------------------------------------------- full sizes
