@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Benchmark of the FlashAttention forward pass on one MI355X.
+"""Benchmark of the FlashAttention forward (and backward) pass on one MI355X.
 
 A step is one call of the C-ABI entry point over one batch of the workload:
 the whole hot path (tile scheduling, Q/K/V loads, both MFMA products, online
@@ -19,7 +19,13 @@ rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same
 counters give for a plain copy of known size), read from profiles/ and only
 when the kernel sources are unchanged since that measurement.
 
+The line also carries ``backward``: the mean time of one fa_bwd call (its
+three launches, one event pair around the call) on the long-context,
+grouped-query, GPT-2-small and BERT-large workloads, in TFLOP/s by the usual
+convention of 2.5 x the forward's FLOPs.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
+    python bench.py --backward-only --workload NAME   time only fa_bwd on NAME (for profiling runs)
     python bench.py --copy-calibration ...     also run a 256 MiB device copy (for PMC scaling)
     python bench.py --summarize-pmc DIR_FETCH DIR_WRITE --workload NAME
                                                write profiles/traffic_<NAME>.json from two PMC runs
@@ -42,6 +48,8 @@ HEADLINE = "gpt2s_causal_bf16_b8h12n1024d64"
 METRIC = "attention fwd TFLOP/s and % of MI355X dense MFMA peak at N=1K–16K, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 2516.6, "fp8": 5033.2}   # dense MFMA peaks of the type the products use
 HBM_GBPS = 8000.0
+BWD_WORKLOADS = ["long_causal_bf16_b1h32n8192d128", "gqa_causal_bf16_b1h32kv8n8192d128",
+                 "gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64"]
 KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_tile.hpp",
                   "exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp",
                   "exact_io_aware_48_amd/csrc/fa_api.hip"]
@@ -106,6 +114,44 @@ def time_workload(w, steps, warmup, settle_s=0.25, graph=False):
     else:
         f = fa.fa_fwd_gqa if gqa else fa.fa_fwd
         launch = lambda: f(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+    return time_launch(launch, steps, warmup, settle_s, graph)
+
+
+def backward_inputs(w):
+    """Device tensors for one backward step of workload w (bf16): q, k, v, the
+    forward's o and lse (computed here by fa_fwd_gqa), dO, the float32
+    gradient outputs and the statistics workspace."""
+    import numpy as np
+    import torch
+    import exact_io_aware_48_amd as fa
+    from workloads import make_grad_output
+    _, q, k, v = device_inputs(w)
+    do = torch.from_numpy(make_grad_output(w).view(np.int16)).cuda().view(torch.bfloat16)
+    o, lse = fa.fa_fwd_gqa(q, k, v, scale=w.softmax_scale, causal=w.causal)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N), dtype=torch.uint8, device="cuda")
+    return q, k, v, o, lse, do, dq, dk, dv, ws
+
+
+def time_backward(w, steps, warmup, settle_s=0.25, graph=False):
+    """Time exactly `steps` calls of fa_bwd (statistics, dK/dV and dQ launches) on workload w."""
+    import exact_io_aware_48_amd as fa
+    q, k, v, o, lse, do, dq, dk, dv, ws = backward_inputs(w)
+    launch = lambda: fa.fa_bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
+                               workspace=ws)
+    return time_launch(launch, steps, warmup, settle_s, graph)
+
+
+def backward_flops(w):
+    """Backward matmul FLOPs by the usual convention: 2.5 x the forward's (five
+    N x N x d products against the forward's two)."""
+    return 2.5 * w.flops
+
+
+def time_launch(launch, steps, warmup, settle_s=0.25, graph=False):
+    import torch
     # untimed: let the clocks settle on this very step, then the W warmup steps
     torch.cuda.synchronize()
     t_end = time.perf_counter() + settle_s
@@ -238,8 +284,8 @@ def summarize_pmc(dir_fetch, dir_write, workload_name, command=""):
     print(json.dumps(res))
 
 
-def summarize_trace(trace_dir, workload_name, command):
-    """Write profiles/kernel_trace_<workload>.txt from a rocprofv3 --kernel-trace --stats run."""
+def summarize_trace(trace_dir, workload_name, command, prefix="kernel_trace"):
+    """Write profiles/<prefix>_<workload>.txt from a rocprofv3 --kernel-trace --stats run."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
@@ -257,7 +303,7 @@ def summarize_trace(trace_dir, workload_name, command):
         lines.append(f"{name:60s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.2f} "
                      f"{float(r['MinNs'])/1e3:10.2f} {float(r['MaxNs'])/1e3:10.2f} {float(r['Percentage']):7.2f}")
     os.makedirs(PROFILES, exist_ok=True)
-    path = os.path.join(PROFILES, f"kernel_trace_{workload_name}.txt")
+    path = os.path.join(PROFILES, f"{prefix}_{workload_name}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -283,16 +329,20 @@ def main():
     ap.add_argument("--settle", type=float, default=0.25, help="seconds of untimed clock-settling steps")
     ap.add_argument("--graph", action="store_true",
                     help="time one HIP graph replay of the K launches instead of eager launches")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward workloads")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only fa_bwd on --workload and print its line (for profiling runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--summary-prefix", default="kernel_trace", help="file name prefix of --summarize-trace")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command)
         return 0
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.workload, args.command)
+        summarize_trace(args.summarize_trace, args.workload, args.command, args.summary_prefix)
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -311,6 +361,12 @@ def main():
     w = by_name(args.workload)
     if args.copy_calibration:
         copy_calibration()
+    if args.backward_only:
+        bt = time_backward(w, args.steps, args.warmup, args.settle, graph=args.graph)
+        print(json.dumps({"backward": w.name, "ms_per_call": round(bt["kernel_ms_mean"], 5),
+                          "tflops_2p5x_convention": round(backward_flops(w) / (bt["kernel_ms_mean"] * 1e-3) / 1e12, 1),
+                          "timing": bt["timing"]}), flush=True)
+        return 0
     t = time_workload(w, args.steps, args.warmup, args.settle, graph=args.graph)
     achieved, peak, ai = line_for(w, t, args.steps, args.warmup)
     value = w.flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
@@ -358,6 +414,17 @@ def main():
                                "kernel_ms_median": round(ot["kernel_ms_median"], 4), "dtype": ow.dtype,
                                "peak": opk}
         line["other_workloads"] = others
+    if not args.no_backward:
+        bwd = {}
+        for name in BWD_WORKLOADS:
+            bw = by_name(name)
+            bt = time_backward(bw, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle, graph=args.graph)
+            tf = backward_flops(bw) / (bt["kernel_ms_mean"] * 1e-3) / 1e12
+            bwd[name] = {"ms_per_call": round(bt["kernel_ms_mean"], 4), "tflops": round(tf, 1),
+                         "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
+                         "flops": "2.5 x forward (five N x N x d products)",
+                         "launches": "statistics, dK/dV, dQ"}
+        line["backward"] = bwd
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
