@@ -17,6 +17,9 @@ Two independent implementations of the same result:
 * ``backward.attention_backward`` -- dQ, dK, dV of the scalar loss sum(dO * O),
   the chain rule of the plain definition written out (with grouped K/V heads);
   ``dq_rows`` / ``dkdv_cols`` restrict it to chosen query rows or keys.
+* ``decode.attention_decode`` -- N_q queries (the last N_q positions) against
+  N_k keys, and ``decode.merge_partials``, the logsumexp merge of attention
+  partials over disjoint key ranges.
 * ``online.attention_online`` -- the blockwise online-softmax recurrence
   (running row max m, running row sum l, rescale of the partial output when m
   grows, one normalisation at the end), for any block sizes.
@@ -30,7 +33,9 @@ from .naive import attention_naive, attention_rows
 from .gqa import attention_gqa, expand_kv
 from .online import attention_online
 from .backward import attention_backward, backward_head, delta_rows, dkdv_cols, dq_rows
+from .decode import attention_decode, attention_decode_gqa, merge_partials, partial_over_keys
 from .compare import errors
 
 __all__ = ["attention_naive", "attention_rows", "attention_gqa", "expand_kv", "attention_online",
-           "attention_backward", "backward_head", "delta_rows", "dq_rows", "dkdv_cols", "errors"]
+           "attention_backward", "backward_head", "delta_rows", "dq_rows", "dkdv_cols",
+           "attention_decode", "attention_decode_gqa", "partial_over_keys", "merge_partials", "errors"]
