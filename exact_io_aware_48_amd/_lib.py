@@ -1,4 +1,4 @@
-"""ctypes view of libfa_fwd.so: the C ABI declared in include/fa_fwd.h and include/fa_bwd.h, nothing else."""
+"""ctypes view of libfa_fwd.so: the C ABI declared in include/fa_fwd.h, fa_bwd.h and fa_split.h, nothing else."""
 
 import ctypes
 import os
@@ -37,6 +37,12 @@ def load():
     lib.fa_bwd_workspace_size.restype = i32
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_fwd_split_plan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, pi, pl]
+    lib.fa_fwd_split_plan.restype = i32
+    lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.fa_fwd_split.restype = i32
+    lib.fa_lse_merge.argtypes = [vp, vp, i64, i64, i64, vp, vp, i32, vp]
+    lib.fa_lse_merge.restype = i32
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i32
     _lib = lib

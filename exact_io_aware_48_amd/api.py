@@ -1,4 +1,4 @@
-"""Python binding of the C ABI (include/fa_fwd.h, include/fa_bwd.h), same names,
+"""Python binding of the C ABI (include/fa_fwd.h, fa_bwd.h, fa_split.h), same names,
 argument marshalling only.
 
 torch supplies device memory and streams; every step of the attention forward
@@ -214,3 +214,68 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
     if st != _lib.FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, num_splits=0):
+    """(splits, workspace bytes) fa_fwd_split would use."""
+    sp, nb = ctypes.c_int(), ctypes.c_int64()
+    st = _lib.load().fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, int(num_splits), _lib.FA_BF16, ctypes.byref(sp),
+                                       ctypes.byref(nb))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_split_plan")
+    return sp.value, nb.value
+
+
+def fa_fwd_split(q, k, v, scale=None, causal=False, num_splits=0, o=None, lse=None, workspace=None, stream=None):
+    """Split-KV attention for decode shapes: q [B, H, N_q, d] (the last N_q positions),
+    k and v [B, H_kv, N_k, d] with N_q <= N_k, all bfloat16.  Returns (o, lse):
+    bfloat16 [B, H, N_q, d] and float32 [B, H, N_q]."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    B, H, N_q, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must both be [B, H_kv, N_k, d] with q's B and d")
+    H_kv, N_k = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _, need = fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds fewer than {need} bytes")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  workspace.data_ptr(), B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)),
+                                  int(num_splits), _lib.FA_BF16, _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_split")
+    return o, lse
+
+
+def fa_lse_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, o=None, lse=None, stream=None):
+    """Merge attention partials: o_parts float32 [S, rows, d], lse_parts float32 [S, rows].
+    Returns (o [rows, d] of out_dtype (bfloat16 or float32), lse float32 [rows])."""
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if o_parts.dim() != 3 or lse_parts.shape != o_parts.shape[:2]:
+        raise ValueError("o_parts must be [S, rows, d] and lse_parts [S, rows]")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()) or o_parts.device.type != "cuda":
+        raise ValueError("partials must be contiguous device tensors")
+    S, rows, d = o_parts.shape
+    code = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_F32}.get(out_dtype)
+    if code is None:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    if o is None:
+        o = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    st = _lib.load().fa_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, rows, d, o.data_ptr(), lse.data_ptr(),
+                                  code, _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_lse_merge")
+    return o, lse

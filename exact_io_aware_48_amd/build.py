@@ -18,9 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_fwd.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "fa_api.hip"), os.path.join(CSRC, "fa_bwd_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fa_api.hip", "fa_bwd_api.hip", "fa_split_api.hip")]
 HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp",
-                                           "fa_host.hpp")] + [os.path.join(INCLUDE, h) for h in ("fa_fwd.h", "fa_bwd.h")]
+                                           "fa_split_kernel.hpp", "fa_host.hpp")] + \
+    [os.path.join(INCLUDE, h) for h in ("fa_fwd.h", "fa_bwd.h", "fa_split.h")]
 
 
 def hipcc():

@@ -1,0 +1,185 @@
+// C ABI of split-KV decode attention and the logsumexp merge (declared in
+// include/fa_split.h): argument checks, split plan, launches.  No
+// allocation, no synchronisation, no state.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "fa_split.h"
+#include "fa_split_kernel.hpp"
+#include "fa_host.hpp"
+
+namespace {
+
+using fa::MergeParams;
+using fa::SplitParams;
+
+// Keys per tile per head dim: one wave per workgroup, 32 KiB of K/V ring, so
+// that five workgroups share a CU and keep enough of the K/V stream in flight.
+int split_bc(int64_t d) { return d == 128 ? 32 : 64; }
+constexpr int kSplitNW = 1;
+constexpr int kRowsPerBlock = 32 * kSplitNW;
+
+struct Plan {
+  int64_t rows_per_head;   // G * N_q
+  int64_t nrb;             // row blocks per K/V head
+  int64_t splits;
+  int64_t chunk;           // keys per split
+  int64_t workspace_bytes;
+};
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return cus;
+}
+
+fa_status check_split_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int dtype) {
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || N_q < 1 || N_k < N_q) return FA_ERR_SHAPE;
+  if (B > INT_MAX / H) return FA_ERR_SHAPE;
+  if (N_k > (int64_t)INT_MAX / (2 * d) || N_q > (int64_t)INT_MAX / (2 * d)) return FA_ERR_SHAPE;
+  if (B * H > INT64_MAX / (N_k * d * 4)) return FA_ERR_SHAPE;
+  if ((H / H_kv) * N_q > INT_MAX / 2) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// The split plan: num_splits > 0 asks for that many (fewer when the tiles run
+// out); 0 picks enough splits for about four workgroups per CU, each split
+// keeping at least four tiles.
+fa_status make_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int num_splits,
+                    int cus, Plan* out) {
+  if (num_splits < 0) return FA_ERR_SHAPE;
+  const int64_t bc = split_bc(d);
+  Plan pl{};
+  pl.rows_per_head = (H / H_kv) * N_q;
+  pl.nrb = (pl.rows_per_head + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t base = B * H_kv * pl.nrb;
+  const int64_t tiles = (N_k + bc - 1) / bc;
+  int64_t want = num_splits;
+  if (want == 0) {
+    want = (4 * (int64_t)cus + base - 1) / base;
+    want = std::max<int64_t>(1, std::min(want, tiles / 4));
+  }
+  want = std::min(want, tiles);
+  const int64_t chunk_tiles = (tiles + want - 1) / want;
+  pl.chunk = chunk_tiles * bc;
+  pl.splits = (tiles + chunk_tiles - 1) / chunk_tiles;
+  if (pl.splits * base > INT_MAX) return FA_ERR_SHAPE;
+  const int64_t rows_total = B * H * N_q;
+  if (rows_total > INT64_MAX / (pl.splits * (d + 1) * 4)) return FA_ERR_SHAPE;
+  pl.workspace_bytes = pl.splits * rows_total * (d + 1) * 4;
+  *out = pl;
+  return FA_OK;
+}
+
+// K/V ring depth.  Measured on MI355X at 2 to 5 stages: decode streams at
+// 5.5-5.8 TB/s whatever the depth (a 1 GiB device copy reaches 5.2), so the
+// plain double buffer is kept.
+constexpr int kSplitNS = 2;
+
+template <int D, bool CAUSAL>
+hipError_t launch_split(const SplitParams& p, int grid, hipStream_t stream) {
+  constexpr int BC = D == 128 ? 32 : 64;
+  void (*kern)(SplitParams) = &fa::fa_split_kernel<D, BC, kSplitNW, kSplitNS, CAUSAL>;
+  SplitParams args = p;
+  void* kargs[] = {&args};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * kSplitNW), kargs, 0, stream);
+}
+
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int64_t S, int64_t rows, int64_t d, void* o,
+                        float* lse, bool out_bf16, hipStream_t stream) {
+  MergeParams mp{};
+  mp.o_part = o_parts;
+  mp.lse_part = lse_parts;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = rows;
+  mp.S = (int)S;
+  mp.d = (int)d;
+  mp.out_bf16 = out_bf16 ? 1 : 0;
+  void* kargs[] = {&mp};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_merge_kernel), dim3((unsigned)((rows + 3) / 4)),
+                         dim3(256), kargs, 0, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int num_splits,
+                            int dtype, int* splits, int64_t* workspace_bytes) {
+  fa_status st = check_split_shape(B, H, H_kv, N_q, N_k, d, dtype);
+  if (st != FA_OK) return st;
+  Plan pl;
+  st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, num_splits == 0 ? device_cus() : 256, &pl);
+  if (st != FA_OK) return st;
+  if (splits) *splits = (int)pl.splits;
+  if (workspace_bytes) *workspace_bytes = pl.workspace_bytes;
+  return FA_OK;
+}
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int64_t B,
+                       int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
+                       int num_splits, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+  fa_status st = check_split_shape(B, H, H_kv, N_q, N_k, d, dtype);
+  if (st != FA_OK) return st;
+  for (const void* ptr : {q, k, v, (const void*)o, (const void*)lse, (const void*)workspace})
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  const double c2 = std::fabs((double)scale) * 1.4426950408889634;
+  if (!std::isfinite((float)c2)) return FA_ERR_SCALE;
+  Plan pl;
+  st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, num_splits == 0 ? device_cus() : 256, &pl);
+  if (st != FA_OK) return st;
+
+  const int64_t rows_total = B * H * N_q;
+  SplitParams p{};
+  p.q = q; p.k = k; p.v = v;
+  p.o_part = static_cast<float*>(workspace);
+  p.lse_part = p.o_part + pl.splits * rows_total * d;
+  p.BHkv = (int)(B * H_kv);
+  p.G = (int)(H / H_kv);
+  p.N_q = (int)N_q;
+  p.N_k = (int)N_k;
+  p.rows = (int)pl.rows_per_head;
+  p.nrb = (int)pl.nrb;
+  p.S = (int)pl.splits;
+  p.chunk = (int)pl.chunk;
+  // masked scores are -inf and rely on c2 > 0 (see fa_api.hip); a negative scale flips Q's sign bits
+  p.c2 = std::max((float)c2, 1e-30f);
+  p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  const int grid = (int)(pl.splits * pl.nrb * B * H_kv);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d == 64) e = causal ? launch_split<64, true>(p, grid, s) : launch_split<64, false>(p, grid, s);
+  else e = causal ? launch_split<128, true>(p, grid, s) : launch_split<128, false>(p, grid, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+  e = launch_merge(p.o_part, p.lse_part, pl.splits, rows_total, d, o, lse, true, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_lse_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t rows, int64_t d,
+                       void* o, float* lse, int out_dtype, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (out_dtype != FA_BF16 && out_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (num_parts < 1 || num_parts > INT_MAX || rows < 1 || d < 1 || d > 4096) return FA_ERR_SHAPE;
+  if ((rows + 3) / 4 > INT_MAX || rows > INT64_MAX / (num_parts * d * 4)) return FA_ERR_SHAPE;
+  for (const void* ptr : {(const void*)o_parts, (const void*)lse_parts, (const void*)o, (const void*)lse})
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const hipError_t e = launch_merge(o_parts, lse_parts, num_parts, rows, d, o, lse, out_dtype == FA_BF16,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Split-KV attention for decode shapes on gfx950, and the logsumexp merge.
+//
+// What it computes: for N_q queries that are the last N_q positions of an
+// N_k-key sequence (query i sees keys j <= N_k - N_q + i under the causal
+// mask), O = softmax(scale * Q K^T) V and L = logsumexp, for grouped K/V
+// heads.  The pages name sequence parallelism among FlashAttention-2's
+// changes (systems-analysis.info "FlashAttention (PL)", section
+// "FlashAttention-2 (2023)") and list decoding work (FlashDecoding++) in its
+// literature; the split over keys with a logsumexp merge is that idea for a
+// sequence too short in queries to fill the GPU.
+//
+// How:
+//   1. fa_split_kernel: a workgroup owns one key range (a split) of one K/V
+//      head and up to 32*NW of its rows, a row being (query head of the
+//      group, query): decode has G * N_q rows per K/V head, so the query
+//      heads that share a K/V stream share one pass over it.  The range's
+//      K/V tiles stream through an LDS ring with the forward's staging and
+//      per-wave pieces (S^T = K Q^T, online softmax, O^T += V^T P^T); the
+//      workgroup writes its partial O_s (normalised over its range, fp32)
+//      and L_s.  A row that sees no key of the range writes O_s = 0,
+//      L_s = -inf.
+//   2. fa_merge_kernel: L = logsumexp_s L_s and O = sum_s exp(L_s - L) O_s per
+//      row, one wave per row.
+#pragma once
+
+#include "fa_tile.hpp"
+
+namespace fa {
+
+struct SplitParams {
+  const void* q;      // bf16 [B][H][N_q][D]
+  const void* k;      // bf16 [B][H_kv][N_k][D]
+  const void* v;
+  float* o_part;      // [S][B*H*N_q][D]
+  float* lse_part;    // [S][B*H*N_q]
+  int BHkv;           // B * H_kv
+  int G;              // query heads per K/V head
+  int N_q, N_k;
+  int rows;           // G * N_q rows per K/V head
+  int nrb;            // row blocks per K/V head
+  int S;              // splits
+  int chunk;          // keys per split, a multiple of the tile
+  float c2;           // |scale| * log2(e)
+  uint32_t qsign;     // XOR mask on Q's sign bits (negative scale)
+};
+
+// Wait until the oldest tile in flight has landed, `more` being how many
+// tiles after it are still to be waited for (at most NS - 2 of them are in
+// flight behind it; loads complete in issue order).
+template <int NS, int LOADS>
+__device__ __forceinline__ void wait_tile(int more) {
+  if constexpr (NS >= 4) {
+    if (more >= 2) { wait_vmcnt<(NS >= 4 ? 2 : 0) * LOADS>(); return; }
+  }
+  if constexpr (NS >= 3) {
+    if (more >= 1) { wait_vmcnt<(NS >= 3 ? 1 : 0) * LOADS>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// NS: depth of the K/V ring (tiles j+1 .. j+NS-1 in flight while tile j is used).
+template <int D, int BC, int NW, int NS, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
+  constexpr int MODE = MODE_BF16;
+  using G = Geo<D, BC, NW, MODE>;
+  using T = Tile<D, BC, NW, MODE>;
+  constexpr int NDB = T::NDB;
+  constexpr int SLOT = 2 * G::SLOTB;                      // K tile then V tile
+  constexpr int LOADS = 2 * G::UPT;                       // DMA instructions per tile per wave
+  static_assert(NS >= 2 && NS * SLOT <= 160 * 1024, "LDS budget");
+  static_assert((NS - 2) * LOADS <= 63, "outstanding loads fit the wait counter");
+
+  __shared__ __attribute__((aligned(16))) char smem_raw[NS * SLOT];
+  char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
+  auto kslot = [&](int s) __attribute__((always_inline)) { return smem + s * SLOT; };
+  auto vslot = [&](int s) __attribute__((always_inline)) { return smem + s * SLOT + G::SLOTB; };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const typename T::Lane ln = T::lane_info(lane);
+
+  const int id = blockIdx.x;
+  const int s = id % p.S;
+  const int rb = (id / p.S) % p.nrb;
+  const int bhk = id / (p.S * p.nrb);
+  const int N_k = p.N_k;
+  const int64_t kv_off = (int64_t)bhk * N_k * D;
+
+  // this lane's row: (query head hh of the group, query i)
+  const int r = rb * G::BR + 32 * wave + ln.n;
+  const bool row_ok = r < p.rows;
+  const int hh = row_ok ? r / p.N_q : 0, qi = row_ok ? r - hh * p.N_q : 0;
+  const int64_t row_g = (int64_t)bhk * p.rows + r;              // = (bhk*G + hh)*N_q + qi
+  typename T::QFrag q;
+  {
+    const int sgn = (int)p.qsign;
+    const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + row_g * D);
+#pragma unroll
+    for (int c = 0; c < T::QK_STEPS; ++c) {
+      i32x4 w = row_ok ? src[2 * c + ln.hf] : i32x4{0, 0, 0, 0};
+      w ^= i32x4{sgn, sgn, sgn, sgn};
+      q.a[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  // key range of this split, and the last key this lane's row sees
+  const int k_lo = s * p.chunk, k_hi = min(N_k, k_lo + p.chunk);
+  const int row_last = CAUSAL ? N_k - p.N_q + qi : N_k - 1;
+  const int last_key = min(row_last, k_hi - 1) - 4 * ln.hf;
+  const int j0 = k_lo / BC, j1 = (k_hi + BC - 1) / BC;
+  const int first_row_last = CAUSAL ? N_k - p.N_q : N_k - 1;   // the smallest limit of any row
+
+  Stager<D, BC, NW, MODE, false> kstage;
+  Stager<D, BC, NW, MODE, true> vstage;
+  kstage.init(wave, lane);
+  vstage.init(wave, lane);
+  const char* kglob = static_cast<const char*>(p.k) + kv_off * 2;
+  const char* vglob = static_cast<const char*>(p.v) + kv_off * 2;
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int b = 0; b < NDB; ++b) oacc[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = p.c2;
+  typename T::PFrag pf;
+
+  // prologue: tiles j0 .. j0+NS-2 in flight, the first one landed
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (j0 + t < j1) {
+      kstage.issue(kglob, j0 + t, N_k, kslot(t), wave, lane);
+      vstage.issue(vglob, j0 + t, N_k, vslot(t), wave, lane);
+    }
+  wait_tile<NS, LOADS>(j1 - j0 - 1);
+  __syncthreads();
+  int cur = 0;
+  for (int j = j0; j < j1; ++j) {
+    // refill the slot tile j-1 used (its readers passed the last barrier)
+    if (j + NS - 1 < j1) {
+      const int slot = cur == 0 ? NS - 1 : cur - 1;
+      kstage.issue(kglob, j + NS - 1, N_k, kslot(slot), wave, lane);
+      vstage.issue(vglob, j + NS - 1, N_k, vslot(slot), wave, lane);
+    }
+    {
+      f32x16 st[T::KB];
+      T::qk(st, kslot(cur), q, ln);
+      const int key0 = j * BC;
+      if ((key0 + BC > k_hi) || (CAUSAL && key0 + BC - 1 > first_row_last)) T::mask(st, last_key - key0);
+      typename T::Softmax sm;
+      T::template softmax_slices<0, T::NMAX + 1>(st, sm, m_run, c2, pf);
+      if (__builtin_amdgcn_ballot_w64(sm.grow)) {
+        asm volatile("" ::: "memory");
+        l_run *= sm.alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) oacc[b] *= sm.alpha;
+      }
+      T::template softmax_slices<T::NMAX + 1, T::NSLICES>(st, sm, m_run, c2, pf);
+      l_run += sm.psum[0] + sm.psum[1];
+      T::pv(oacc, vslot(cur), pf, ln);
+    }
+    wait_tile<NS, LOADS>(j1 - j - 2);                     // tile j+1 has landed
+    __syncthreads();
+    cur = cur + 1 == NS ? 0 : cur + 1;
+  }
+
+  const float l_tot = swap_halves_sum(l_run);
+  if (!row_ok) return;
+  const int64_t prow = (int64_t)s * p.BHkv * p.rows + row_g;   // row of this split's partial
+  const bool seen = l_tot > 0.f;
+  const float inv = seen ? 1.f / l_tot : 0.f;
+  if (ln.hf == 0) p.lse_part[prow] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  float* dst = p.o_part + prow * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * db + 8 * g + 4 * ln.hf;
+      *reinterpret_cast<f32x4*>(dst + col) = f32x4{oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
+                                                   oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+    }
+}
+
+struct MergeParams {
+  const float* o_part;   // [S][rows][d]
+  const float* lse_part; // [S][rows]
+  void* o;               // [rows][d], bf16 or fp32
+  float* lse;            // [rows]
+  int64_t rows;
+  int S, d;
+  int out_bf16;
+};
+
+// One wave per row; lane t handles dims t, t + 64, ...
+__global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < p.S; ++s) m = fmaxf(m, p.lse_part[(int64_t)s * p.rows + row]);
+  const float m_use = m == -INFINITY ? 0.f : m;
+  float tot = 0.f;
+  for (int s = 0; s < p.S; ++s) tot += __expf(p.lse_part[(int64_t)s * p.rows + row] - m_use);
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  if (lane == 0) p.lse[row] = tot > 0.f ? m_use + __logf(tot) : -INFINITY;
+  for (int c = lane; c < p.d; c += 64) {
+    float acc = 0.f;
+    for (int s = 0; s < p.S; ++s) {
+      const float w = __expf(p.lse_part[(int64_t)s * p.rows + row] - m_use);
+      acc = __builtin_fmaf(w, p.o_part[((int64_t)s * p.rows + row) * p.d + c], acc);
+    }
+    const float x = acc * inv;
+    if (p.out_bf16) {
+      static_cast<uint16_t*>(p.o)[row * p.d + c] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+    } else {
+      static_cast<float*>(p.o)[row * p.d + c] = x;
+    }
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,87 @@
+/*
+ * fa_split.h -- C ABI of split-KV (decode-shaped) attention and the
+ * logsumexp merge of attention partials, for MI355X (gfx950).
+ *
+ * Operation.  N_q queries that are the last N_q positions of a sequence of
+ * N_k >= N_q keys: for batch b and query head h (K/V head h / (H / H_kv)),
+ *
+ *     O   = softmax(S) V,   lse = log(sum_j exp(S_ij)),   S = scale * Q K^T,
+ *
+ * where under the causal mask query i (0-based among the N_q) sees keys
+ * j <= N_k - N_q + i (N_q = N_k is the square mask of fa_fwd).  The key
+ * range is split over workgroups; each split writes a partial (O_s
+ * normalised over its keys, L_s its logsumexp) and a merge forms
+ *
+ *     L = log(sum_s exp(L_s)),   O = sum_s exp(L_s - L) O_s,
+ *
+ * which is the exact softmax over all keys.  The pages name sequence
+ * parallelism among FlashAttention-2's changes (systems-analysis.info
+ * "FlashAttention (PL)", section "FlashAttention-2 (2023)") and cite decoding
+ * work (FlashDecoding++) in its literature list; they give no formula, so
+ * this is the attention definition of fa_fwd.h over the keys each query sees.
+ *
+ * Layout.  q, o: dense [B][H][N_q][d]; k, v: [B][H_kv][N_k][d]; lse:
+ * float32 [B][H][N_q].  Memory, streams, re-entrancy and errors as in
+ * fa_fwd.h.  The result depends on the number of splits only through
+ * rounding; for a fixed split count it is bitwise reproducible.
+ */
+#ifndef FA_SPLIT_H
+#define FA_SPLIT_H
+
+#include <stdint.h>
+
+#include "fa_fwd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * fa_fwd_split_plan -- the split count fa_fwd_split would use and the
+ * workspace it needs (splits * B * H * N_q * (d + 1) * 4 bytes), without
+ * launching anything.  num_splits = 0 lets the library choose (about four
+ * workgroups per compute unit of the current device, at least four 32- or
+ * 64-key tiles per split); a positive value asks for that many splits, fewer
+ * when the key tiles run out.  splits and workspace_bytes may be NULL.
+ * Checks as fa_fwd_split (FA_ERR_SHAPE also for num_splits < 0).
+ */
+fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d,
+                            int num_splits, int dtype, int* splits, int64_t* workspace_bytes);
+
+/*
+ * fa_fwd_split -- O and lse as above, by split-KV partials and their merge
+ * (two launches).
+ *   q          : bfloat16 [B][H][N_q][d]
+ *   k, v       : bfloat16 [B][H_kv][N_k][d]
+ *   o          : bfloat16 output [B][H][N_q][d]
+ *   lse        : float32 output [B][H][N_q]
+ *   workspace  : device memory of the size fa_fwd_split_plan reports for the
+ *                same arguments; holds the partials (fp32 O_s, then L_s)
+ *   N_q, N_k   : 1 <= N_q <= N_k, else FA_ERR_SHAPE
+ *   d          : 64 or 128; dtype must be FA_BF16 (else FA_ERR_UNSUPPORTED)
+ *   scale      : any finite value; causal as described above
+ *   num_splits : as for fa_fwd_split_plan
+ * Every pointer must be 16-byte aligned.
+ */
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                       int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d,
+                       float scale, int causal, int num_splits, int dtype, void* stream);
+
+/*
+ * fa_lse_merge -- the merge alone, for partials made elsewhere (for example
+ * one per device of a sequence-parallel split):
+ *   o_parts   : float32 [num_parts][rows][d], each part normalised over its keys
+ *   lse_parts : float32 [num_parts][rows]; -inf marks a part the row does not see
+ *               (its O part is then ignored)
+ *   o         : output [rows][d], bfloat16 (out_dtype FA_BF16) or float32 (FA_F32)
+ *   lse       : float32 output [rows]; -inf (and O = 0) for a row no part sees
+ * 1 <= num_parts, 1 <= rows, 1 <= d <= 4096, else FA_ERR_SHAPE.
+ */
+fa_status fa_lse_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t rows,
+                       int64_t d, void* o, float* lse, int out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_SPLIT_H */

@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa",
-                                    "fa_fwd_gqa_fp8", "fa_plan", "fa_status_string", "fa_version"]
+                                    "fa_fwd_gqa_fp8", "fa_fwd_split", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
+                                    "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -149,3 +150,56 @@ def _bwd_args(**kw):
 ])
 def test_fa_bwd_validation(lib, kw, expected):
     assert lib.fa_bwd(*_bwd_args(**kw)) == expected
+
+
+def _plan(lib, B, H, H_kv, N_q, N_k, d, splits, dtype=1):
+    sp, nb = ctypes.c_int(), ctypes.c_int64()
+    st = lib.fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, splits, dtype, ctypes.byref(sp), ctypes.byref(nb))
+    return st, sp.value, nb.value
+
+
+def test_fa_fwd_split_plan(lib):
+    # asked-for splits: 8192 keys in 32-key tiles (d = 128) -> 8 splits of 1024 keys
+    st, sp, nb = _plan(lib, 2, 32, 8, 1, 8192, 128, 8)
+    assert st == 0 and sp == 8 and nb == 8 * 2 * 32 * 1 * 129 * 4
+    # more splits than tiles: one per tile
+    st, sp, _ = _plan(lib, 1, 4, 4, 1, 100, 64, 50)
+    assert st == 0 and sp == 2
+    # 10 tiles over 3 requested splits: chunks of 4 tiles -> 3 splits
+    st, sp, _ = _plan(lib, 1, 1, 1, 1, 640, 64, 3)
+    assert st == 0 and sp == 3
+    # automatic: at least one, never more than a quarter of the tiles
+    st, sp, _ = _plan(lib, 1, 8, 8, 1, 100, 64, 0)
+    assert st == 0 and sp == 1
+    st, sp, _ = _plan(lib, 1, 8, 1, 1, 65536, 128, 0)
+    assert st == 0 and 1 <= sp <= 2048 // 4
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((1, 8, 3, 1, 64, 64, 0), 2), ((1, 8, 8, 0, 64, 64, 0), 2), ((1, 8, 8, 65, 64, 64, 0), 2),
+    ((1, 8, 8, 1, 64, 64, -1), 2), ((1, 8, 8, 1, 64, 256, 0), 3), ((1, 8, 8, 1, 64, 64, 0, 0), 3),
+])
+def test_fa_fwd_split_plan_validation(lib, args, expected):
+    assert _plan(lib, *args)[0] == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"q": 0}, 1), ({"ws": 0}, 1), ({"N_q": 5, "N_k": 4}, 2), ({"H_kv": 3}, 2), ({"d": 256}, 3), ({"dtype": 0}, 3),
+    ({"o": FAKE + 2}, 4), ({"ws": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
+])
+def test_fa_fwd_split_validation(lib, kw, expected):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, B=1, H=4, H_kv=2, N_q=1, N_k=64, d=64, scale=0.1,
+             causal=0, splits=0, dtype=1)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "ws", "B", "H", "H_kv", "N_q", "N_k", "d", "scale", "causal",
+                           "splits", "dtype")] + [None]
+    assert lib.fa_fwd_split(*args) == expected
+
+
+@pytest.mark.parametrize("args,expected", [
+    ((0, FAKE, 2, 4, 64, FAKE, FAKE, 1), 1), ((FAKE, FAKE, 0, 4, 64, FAKE, FAKE, 1), 2),
+    ((FAKE, FAKE, 2, 0, 64, FAKE, FAKE, 1), 2), ((FAKE, FAKE, 2, 4, 5000, FAKE, FAKE, 1), 2),
+    ((FAKE, FAKE, 2, 4, 64, FAKE, FAKE, 2), 3), ((FAKE, FAKE + 4, 2, 4, 64, FAKE, FAKE, 1), 4),
+])
+def test_fa_lse_merge_validation(lib, args, expected):
+    assert lib.fa_lse_merge(*args, None) == expected

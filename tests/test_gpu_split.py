@@ -1,0 +1,124 @@
+"""GPU parity of split-KV decode attention (fa_fwd_split) and of the merge
+(fa_lse_merge) against the float64 oracle (oracle/decode.py).
+
+Inputs are the seeded bf16 bytes of ``workloads``.  O is compared element by
+element at the forward's bf16 tolerances (max abs 2e-2, relative L2 5e-3,
+lse 1e-3); the merge alone is compared on partials the oracle made from a
+real key split.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_decode_gqa, errors, merge_partials, partial_over_keys
+from workloads import DECODE_WORKLOADS, by_name, make_inputs
+
+from gpu_util import TOL, check, to_device
+
+pytestmark = pytest.mark.gpu
+BASE = "decode_gqa_bf16_b8h32kv8q1n32768d128"
+
+
+def _print_case(*a):
+    print("CASE split", *a, flush=True)
+
+
+def run_split(x, splits=0, scale=None):
+    import exact_io_aware_48_amd as fa
+    w = x.workload
+    q, k, v = to_device(x)
+    o, lse = fa.fa_fwd_split(q, k, v, scale=w.softmax_scale if scale is None else scale, causal=w.causal,
+                             num_splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle(x, scale=None):
+    w = x.workload
+    return attention_decode_gqa(x.f64("q"), x.f64("k"), x.f64("v"), w.softmax_scale if scale is None else scale,
+                                w.causal)
+
+
+CASES = [
+    # (B, H, H_kv, N_q, N_k, d, causal, splits)
+    (2, 8, 2, 1, 1000, 128, True, 0),
+    (1, 32, 8, 1, 4096, 128, False, 0),
+    (1, 4, 1, 3, 777, 64, True, 5),
+    (2, 6, 3, 16, 2048, 64, True, 0),
+    (1, 8, 8, 1, 100, 128, False, 1),
+    (1, 2, 2, 64, 64, 128, True, 2),          # square: the forward's causal mask
+    (1, 4, 2, 1, 20, 64, True, 0),            # fewer keys than one tile
+    (1, 16, 2, 8, 500, 128, True, 3),         # 64 rows per K/V head: two row blocks
+    (1, 2, 1, 1, 100, 64, True, 1000),        # more splits asked than tiles
+    (3, 4, 4, 2, 3000, 64, False, 7),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_q,N_k,d,causal,splits", CASES)
+def test_split_all_elements(B, H, H_kv, N_q, N_k, d, causal, splits):
+    _print_case(B, H, H_kv, N_q, N_k, d, causal, splits)
+    w = by_name(BASE).with_(B=B, H=H, H_kv=H_kv, N_q=N_q, N=N_k, d=d, causal=causal, seed=100 + N_k)
+    x = make_inputs(w)
+    o, l = run_split(x, splits)
+    o_ref, l_ref = oracle(x)
+    check(errors(o, o_ref, l, l_ref), "bf16", f"split B={B} H={H}/{H_kv} N_q={N_q} N_k={N_k} d={d} S={splits}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.7])
+def test_split_other_scales(scale):
+    _print_case("scale", scale)
+    w = by_name(BASE).with_(B=1, H=8, H_kv=2, N_q=4, N=900, d=128, seed=5)
+    x = make_inputs(w)
+    o, l = run_split(x, 0, scale)
+    o_ref, l_ref = oracle(x, scale)
+    check(errors(o, o_ref, l, l_ref), "bf16", f"scale {scale}")
+
+
+def test_split_count_changes_only_rounding_and_repeats_bitwise():
+    _print_case("splits")
+    w = by_name(BASE).with_(B=1, H=8, H_kv=2, N_q=2, N=5000, d=128, seed=6)
+    x = make_inputs(w)
+    o_ref, l_ref = oracle(x)
+    runs = {}
+    for s in (1, 4, 0, 40):
+        runs[s] = run_split(x, s)
+        check(errors(*runs[s][:1], o_ref, runs[s][1], l_ref), "bf16", f"splits {s}")
+    again = run_split(x, 4)
+    assert np.array_equal(again[0], runs[4][0]) and np.array_equal(again[1], runs[4][1])
+
+
+@pytest.mark.parametrize("w", DECODE_WORKLOADS, ids=lambda w: w.name)
+def test_split_full_size_all_elements(w):
+    _print_case("full", w.name)
+    x = make_inputs(w)
+    o, l = run_split(x)
+    o_ref, l_ref = oracle(x)
+    check(errors(o, o_ref, l, l_ref), "bf16", w.name)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_entry_point(out_dtype):
+    import exact_io_aware_48_amd as fa
+    _print_case("merge", out_dtype)
+    rng = np.random.default_rng(9)
+    rows, d, N_k = 24, 96, 300
+    q, k, v = rng.standard_normal((rows, d)), rng.standard_normal((N_k, d)), rng.standard_normal((N_k, d))
+    cuts = [0, 7, 7, 150, 299, 300]                    # one empty part, one single key
+    parts = [partial_over_keys(q, k, v, 0.1, True, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    o_parts = np.stack([p[0] for p in parts]).astype(np.float32)
+    l_parts = np.stack([p[1] for p in parts]).astype(np.float32)
+    o_ref, l_ref = merge_partials(o_parts.astype(np.float64), l_parts.astype(np.float64))
+    o, l = fa.fa_lse_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(l_parts).cuda(), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    tol = 1e-5 if out_dtype == torch.float32 else 8e-3
+    assert np.max(np.abs(o - o_ref)) <= tol * max(1.0, np.max(np.abs(o_ref)))
+    assert np.max(np.abs(l - l_ref)) <= 1e-5 * max(1.0, np.max(np.abs(l_ref)))
+    # a row no part sees merges to O = 0, L = -inf
+    l_parts[:, 3] = -np.inf
+    o2, l2 = fa.fa_lse_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(l_parts).cuda(),
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.isneginf(l2.cpu().numpy()[3]) and np.all(o2.cpu().numpy()[3] == 0)

@@ -16,15 +16,17 @@ Recipe (one workload = one seed):
     e4m3fn (round-to-nearest-even, saturating at +-448).  The kernel receives
     the e4m3 bytes plus s as a "descale"; the oracle receives the dequantised
     values x8 * s exactly, in float64.
+  * Decode workloads (``N_q`` set) draw Q as [B, H, N_q, d] and K, V as
+    [B, H_kv, N, d], in the same order.
   * The backward's upstream gradient dO is drawn the same way from
     ``default_rng(seed + 7919)`` and rounded to bfloat16 (``make_grad_output``).
 """
 
 from .encode import (bf16_bits_from_f32, bf16_bits_to_f64, e4m3fn_bits_from_f32,
                      e4m3fn_bits_to_f64, E4M3FN_MAX)
-from .gen import Workload, WORKLOADS, by_name, make_inputs, make_grad_output, AttnInputs
+from .gen import Workload, WORKLOADS, DECODE_WORKLOADS, by_name, make_inputs, make_grad_output, AttnInputs
 
 __all__ = [
     "bf16_bits_from_f32", "bf16_bits_to_f64", "e4m3fn_bits_from_f32", "e4m3fn_bits_to_f64",
-    "E4M3FN_MAX", "Workload", "WORKLOADS", "by_name", "make_inputs", "make_grad_output", "AttnInputs",
+    "E4M3FN_MAX", "Workload", "WORKLOADS", "DECODE_WORKLOADS", "by_name", "make_inputs", "make_grad_output", "AttnInputs",
 ]

@@ -30,6 +30,7 @@ class Workload:
     seed: int
     scale: float = None  # default 1/sqrt(d)
     H_kv: int = None     # K/V heads (grouped-query attention); default H
+    N_q: int = None      # query rows (decode shape: the last N_q of N keys); default N
 
     @property
     def softmax_scale(self):
@@ -40,13 +41,20 @@ class Workload:
         return self.H if self.H_kv is None else self.H_kv
 
     @property
+    def q_rows(self):
+        return self.N if self.N_q is None else self.N_q
+
+    @property
     def group(self):
         """Query heads per K/V head; query head h reads K/V head h // group."""
         return self.H // self.kv_heads
 
     @property
     def flops(self):
-        """Matmul FLOPs by the usual convention 4*B*H*N^2*d, halved for causal."""
+        """Matmul FLOPs by the usual convention 4*B*H*N^2*d, halved for causal
+        (decode shape: 4*B*H*N_q*N*d, the mask removing almost nothing)."""
+        if self.N_q is not None:
+            return 4.0 * self.B * self.H * self.N_q * self.N * self.d
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
@@ -61,7 +69,7 @@ class Workload:
     @property
     def compulsory_bytes(self):
         """Q, K, V read once; O and the fp32 logsumexp written once."""
-        n = self.B * self.H * self.N
+        n = self.B * self.H * self.q_rows
         nkv = self.B * self.kv_heads * self.N
         return (n + 2 * nkv) * self.d * self.elem_bytes + n * self.d * self.out_elem_bytes + 4 * n
 
@@ -81,8 +89,15 @@ WORKLOADS = [
 ]
 
 
+# decode shapes (split-KV): one new token per sequence against a long cache
+DECODE_WORKLOADS = [
+    Workload("decode_gqa_bf16_b8h32kv8q1n32768d128", 8, 32, 32768, 128, "bf16", True, seed=7, H_kv=8, N_q=1),
+    Workload("decode_mha_bf16_b4h32q1n16384d128", 4, 32, 16384, 128, "bf16", True, seed=8, N_q=1),
+]
+
+
 def by_name(name):
-    for w in WORKLOADS:
+    for w in WORKLOADS + DECODE_WORKLOADS:
         if w.name == name:
             return w
     raise KeyError(name)
@@ -118,10 +133,10 @@ class AttnInputs:
         return e4m3fn_bits_to_f64(x) * float(self.descale[s])
 
 
-def _draw(B, H, N, d, seed, H_kv=None):
+def _draw(B, H, N, d, seed, H_kv=None, N_q=None):
     rng = np.random.default_rng(seed)
     kv_shape = (B, H if H_kv is None else H_kv, N, d)
-    q = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    q = rng.standard_normal((B, H, N if N_q is None else N_q, d), dtype=np.float32)
     k = rng.standard_normal(kv_shape, dtype=np.float32)
     v = rng.standard_normal(kv_shape, dtype=np.float32)
     return q, k, v
@@ -138,7 +153,7 @@ def quantize_e4m3_per_tensor(x32):
 def make_inputs(w, seed=None):
     """Draw the inputs of workload ``w`` (optionally with another seed)."""
     seed = w.seed if seed is None else seed
-    q, k, v = _draw(w.B, w.H, w.N, w.d, seed, w.kv_heads)
+    q, k, v = _draw(w.B, w.H, w.N, w.d, seed, w.kv_heads, w.N_q)
     if w.dtype == "f32":
         return AttnInputs(w, q, k, v)
     qb, kb, vb = bf16_bits_from_f32(q), bf16_bits_from_f32(k), bf16_bits_from_f32(v)
@@ -176,4 +191,4 @@ def make_grad_output(w, seed=None):
     apart from the workload's Q, K, V), rounded to bfloat16."""
     seed = w.seed if seed is None else seed
     rng = np.random.default_rng(seed + 7919)
-    return bf16_bits_from_f32(rng.standard_normal((w.B, w.H, w.N, w.d), dtype=np.float32))
+    return bf16_bits_from_f32(rng.standard_normal((w.B, w.H, w.q_rows, w.d), dtype=np.float32))
