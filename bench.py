@@ -24,6 +24,10 @@ three launches, one event pair around the call) on the long-context,
 grouped-query, GPT-2-small and BERT-large workloads, in TFLOP/s by the usual
 convention of 2.5 x the forward's FLOPs.
 
+It also carries ``decode``: one fa_fwd_split call (split kernel and merge) on
+the decode workloads, as HBM bandwidth over the compulsory bytes (K and V
+read once) against the 8 TB/s peak.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
     python bench.py --backward-only --workload NAME   time only fa_bwd on NAME (for profiling runs)
     python bench.py --copy-calibration ...     also run a 256 MiB device copy (for PMC scaling)
@@ -142,6 +146,21 @@ def time_backward(w, steps, warmup, settle_s=0.25, graph=False):
     launch = lambda: fa.fa_bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
                                workspace=ws)
     return time_launch(launch, steps, warmup, settle_s, graph)
+
+
+def time_decode(w, steps, warmup, settle_s=0.25, graph=False):
+    """Time exactly `steps` calls of fa_fwd_split (split kernel + merge) on decode workload w."""
+    import torch
+    import exact_io_aware_48_amd as fa
+    _, q, k, v = device_inputs(w)
+    splits, nbytes = fa.fa_fwd_split_plan(w.B, w.H, w.kv_heads, w.q_rows, w.N, w.d, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.q_rows), dtype=torch.float32, device="cuda")
+    launch = lambda: fa.fa_fwd_split(q, k, v, scale=w.softmax_scale, causal=w.causal, o=o, lse=lse, workspace=ws)
+    t = time_launch(launch, steps, warmup, settle_s, graph)
+    t["splits"] = splits
+    return t
 
 
 def backward_flops(w):
@@ -330,6 +349,7 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time one HIP graph replay of the K launches instead of eager launches")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward workloads")
+    ap.add_argument("--no-decode", action="store_true", help="skip timing the split-KV decode workloads")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only fa_bwd on --workload and print its line (for profiling runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -425,6 +445,17 @@ def main():
                          "flops": "2.5 x forward (five N x N x d products)",
                          "launches": "statistics, dK/dV, dQ"}
         line["backward"] = bwd
+    if not args.no_decode:
+        from workloads import DECODE_WORKLOADS
+        dec = {}
+        for dw in DECODE_WORKLOADS:
+            dt = time_decode(dw, max(20, args.steps // 2), max(5, args.warmup), args.settle, graph=args.graph)
+            gbs = dw.compulsory_bytes / (dt["kernel_ms_mean"] * 1e-3) / 1e9
+            dec[dw.name] = {"us_per_call": round(dt["kernel_ms_mean"] * 1e3, 1), "splits": dt["splits"],
+                            "hbm_gbs": round(gbs, 0), "frac_of_hbm_peak": round(gbs / HBM_GBPS, 4),
+                            "compulsory_bytes": dw.compulsory_bytes,
+                            "launches": "split kernel, merge"}
+        line["decode"] = dec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

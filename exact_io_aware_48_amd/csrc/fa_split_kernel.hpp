@@ -123,27 +123,38 @@ __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
   const float c2 = p.c2;
   typename T::PFrag pf;
 
-  // prologue: tiles j0 .. j0+NS-2 in flight, the first one landed
+  // Tile t of the range is tile j0 + (t + rot) % nt: every workgroup starts at
+  // a different place in its range, so that workgroups whose ranges lie a
+  // power of two apart do not stream the same HBM channels in lock step.  The
+  // online softmax does not depend on the order of the tiles beyond rounding.
+  const int nt = j1 - j0;
+  const int rot = nt > 0 ? (s + bhk) % nt : 0;
+  auto tile_of = [&](int t) __attribute__((always_inline)) {
+    const int u = t + rot;
+    return j0 + (u >= nt ? u - nt : u);
+  };
+
+  // prologue: tiles 0 .. NS-2 of the range in flight, the first one landed
 #pragma unroll
   for (int t = 0; t < NS - 1; ++t)
-    if (j0 + t < j1) {
-      kstage.issue(kglob, j0 + t, N_k, kslot(t), wave, lane);
-      vstage.issue(vglob, j0 + t, N_k, vslot(t), wave, lane);
+    if (t < nt) {
+      kstage.issue(kglob, tile_of(t), N_k, kslot(t), wave, lane);
+      vstage.issue(vglob, tile_of(t), N_k, vslot(t), wave, lane);
     }
-  wait_tile<NS, LOADS>(j1 - j0 - 1);
+  wait_tile<NS, LOADS>(nt - 1);
   __syncthreads();
   int cur = 0;
-  for (int j = j0; j < j1; ++j) {
-    // refill the slot tile j-1 used (its readers passed the last barrier)
-    if (j + NS - 1 < j1) {
+  for (int t = 0; t < nt; ++t) {
+    // refill the slot tile t-1 used (its readers passed the last barrier)
+    if (t + NS - 1 < nt) {
       const int slot = cur == 0 ? NS - 1 : cur - 1;
-      kstage.issue(kglob, j + NS - 1, N_k, kslot(slot), wave, lane);
-      vstage.issue(vglob, j + NS - 1, N_k, vslot(slot), wave, lane);
+      kstage.issue(kglob, tile_of(t + NS - 1), N_k, kslot(slot), wave, lane);
+      vstage.issue(vglob, tile_of(t + NS - 1), N_k, vslot(slot), wave, lane);
     }
     {
       f32x16 st[T::KB];
       T::qk(st, kslot(cur), q, ln);
-      const int key0 = j * BC;
+      const int key0 = tile_of(t) * BC;
       if ((key0 + BC > k_hi) || (CAUSAL && key0 + BC - 1 > first_row_last)) T::mask(st, last_key - key0);
       typename T::Softmax sm;
       T::template softmax_slices<0, T::NMAX + 1>(st, sm, m_run, c2, pf);
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
       l_run += sm.psum[0] + sm.psum[1];
       T::pv(oacc, vslot(cur), pf, ln);
     }
-    wait_tile<NS, LOADS>(j1 - j - 2);                     // tile j+1 has landed
+    wait_tile<NS, LOADS>(nt - t - 2);                     // tile t+1 has landed
     __syncthreads();
     cur = cur + 1 == NS ? 0 : cur + 1;
   }

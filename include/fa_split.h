@@ -39,7 +39,7 @@ extern "C" {
 /*
  * fa_fwd_split_plan -- the split count fa_fwd_split would use and the
  * workspace it needs (splits * B * H * N_q * (d + 1) * 4 bytes), without
- * launching anything.  num_splits = 0 lets the library choose (about four
+ * launching anything.  num_splits = 0 lets the library choose (about two
  * workgroups per compute unit of the current device, at least four 32- or
  * 64-key tiles per split); a positive value asks for that many splits, fewer
  * when the key tiles run out.  splits and workspace_bytes may be NULL.
