@@ -20,6 +20,8 @@ Two independent implementations of the same result:
 * ``decode.attention_decode`` -- N_q queries (the last N_q positions) against
   N_k keys, and ``decode.merge_partials``, the logsumexp merge of attention
   partials over disjoint key ranges.
+* ``masks.attention_alibi`` / ``masks.attention_blocksparse`` -- the plain
+  definition with ALiBi linear biases or a block-sparse mask.
 * ``online.attention_online`` -- the blockwise online-softmax recurrence
   (running row max m, running row sum l, rescale of the partial output when m
   grows, one normalisation at the end), for any block sizes.
@@ -34,8 +36,10 @@ from .gqa import attention_gqa, expand_kv
 from .online import attention_online
 from .backward import attention_backward, backward_head, delta_rows, dkdv_cols, dq_rows
 from .decode import attention_decode, attention_decode_gqa, merge_partials, partial_over_keys
+from .masks import attention_alibi, attention_biased, attention_blocksparse, expand_block_mask
 from .compare import errors
 
 __all__ = ["attention_naive", "attention_rows", "attention_gqa", "expand_kv", "attention_online",
            "attention_backward", "backward_head", "delta_rows", "dq_rows", "dkdv_cols",
-           "attention_decode", "attention_decode_gqa", "partial_over_keys", "merge_partials", "errors"]
+           "attention_decode", "attention_decode_gqa", "partial_over_keys", "merge_partials",
+           "attention_alibi", "attention_biased", "attention_blocksparse", "expand_block_mask", "errors"]
