@@ -24,7 +24,10 @@ three launches, one event pair around the call) on the long-context,
 grouped-query, GPT-2-small and BERT-large workloads, in TFLOP/s by the usual
 convention of 2.5 x the forward's FLOPs.
 
-It also carries ``decode``: one fa_fwd_split call (split kernel and merge) on
+It also carries ``variants``: ALiBi on the long-context and GPT-2-small
+workloads (TFLOP/s by the plain convention) and a block-sparse sliding
+window with one global block (TFLOP/s over the allowed query/key pairs,
+and the speed-up over the dense kernel).  And ``decode``: one fa_fwd_split call (split kernel and merge) on
 the decode workloads, as HBM bandwidth over the compulsory bytes (K and V
 read once) against the 8 TB/s peak.
 
@@ -161,6 +164,57 @@ def time_decode(w, steps, warmup, settle_s=0.25, graph=False):
     t = time_launch(launch, steps, warmup, settle_s, graph)
     t["splits"] = splits
     return t
+
+
+def alibi_slopes(H):
+    """The geometric slopes 2^(-8 (h + 1) / H) of the ALiBi paper."""
+    return [2.0 ** (-8.0 * (h + 1) / H) for h in range(H)]
+
+
+def time_alibi(w, steps, warmup, settle_s=0.25, graph=False):
+    import torch
+    import exact_io_aware_48_amd as fa
+    _, q, k, v = device_inputs(w)
+    slopes = torch.tensor(alibi_slopes(w.H), dtype=torch.float32, device="cuda")
+    o, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    launch = lambda: fa.fa_fwd_alibi(q, k, v, slopes, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+    return time_launch(launch, steps, warmup, settle_s, graph)
+
+
+def local_global_mask(N, window=1):
+    """Block mask [nb, nb]: each query block sees its neighbours within `window`
+    blocks and the first block (a sliding window with one global block)."""
+    import numpy as np
+    nb = (N + 127) // 128
+    m = np.zeros((nb, nb), dtype=np.uint8)
+    for i in range(nb):
+        m[i, max(0, i - window):i + window + 1] = 1
+        m[i, 0] = 1
+    return m
+
+
+def blocksparse_flops(w, bm):
+    """4*d per allowed (query, key) pair, counted per block pair (ragged edges, causal)."""
+    nb = bm.shape[-1]
+    size = lambda i: min(128, w.N - 128 * i)
+    pairs = 0
+    for i in range(nb):
+        for j in range(nb):
+            if not bm[i, j] or (w.causal and j > i):
+                continue
+            r, c = size(i), size(j)
+            pairs += r * (r + 1) // 2 if (w.causal and i == j) else r * c
+    return 4.0 * w.d * pairs * w.B * w.H
+
+
+def time_blocksparse(w, bm, steps, warmup, settle_s=0.25, graph=False):
+    import torch
+    import exact_io_aware_48_amd as fa
+    _, q, k, v = device_inputs(w)
+    m = torch.from_numpy(bm).cuda()
+    o, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    launch = lambda: fa.fa_fwd_blocksparse(q, k, v, m, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+    return time_launch(launch, steps, warmup, settle_s, graph)
 
 
 def backward_flops(w):
@@ -350,6 +404,7 @@ def main():
                     help="time one HIP graph replay of the K launches instead of eager launches")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the split-KV decode workloads")
+    ap.add_argument("--no-variants", action="store_true", help="skip timing the ALiBi and block-sparse variants")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only fa_bwd on --workload and print its line (for profiling runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -445,6 +500,27 @@ def main():
                          "flops": "2.5 x forward (five N x N x d products)",
                          "launches": "statistics, dK/dV, dQ"}
         line["backward"] = bwd
+    if not args.no_variants:
+        var = {}
+        for name in ("long_causal_bf16_b1h32n8192d128", "gpt2s_causal_bf16_b8h12n1024d64"):
+            vw = by_name(name)
+            at = time_alibi(vw, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle, graph=args.graph)
+            tf = vw.flops / (at["kernel_ms_mean"] * 1e-3) / 1e12
+            var["alibi:" + name] = {"ms_per_call": round(at["kernel_ms_mean"], 4), "tflops": round(tf, 1),
+                                    "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}
+        sw = by_name("long_causal_bf16_b1h32n8192d128").with_(causal=False)
+        bm = local_global_mask(sw.N)
+        bt = time_blocksparse(sw, bm, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle,
+                              graph=args.graph)
+        dt = time_workload(sw, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle, graph=args.graph)
+        tf = blocksparse_flops(sw, bm) / (bt["kernel_ms_mean"] * 1e-3) / 1e12
+        var["blocksparse:local_global_b1h32n8192d128"] = {
+            "ms_per_call": round(bt["kernel_ms_mean"], 4), "tflops_effective": round(tf, 1),
+            "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
+            "density": round(float(bm.mean()), 4), "dense_ms": round(dt["kernel_ms_mean"], 4),
+            "speedup_vs_dense": round(dt["kernel_ms_mean"] / bt["kernel_ms_mean"], 2),
+            "pattern": "each 128-query block sees its neighbours (window 1) and the first key block; non-causal"}
+        line["variants"] = var
     if not args.no_decode:
         from workloads import DECODE_WORKLOADS
         dec = {}

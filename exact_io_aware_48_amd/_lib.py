@@ -33,6 +33,10 @@ def load():
     lib.fa_plan.restype = i32
     lib.fa_status_string.argtypes = [i32]
     lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.fa_fwd_alibi.restype = i32
+    lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, vp]
+    lib.fa_fwd_blocksparse.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, pl]
     lib.fa_bwd_workspace_size.restype = i32
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]

@@ -168,6 +168,63 @@ def fa_fwd_gqa_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None
     return o, lse
 
 
+def _bf16_square(q, k, v):
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    return q.shape
+
+
+def fa_fwd_alibi(q, k, v, slopes, o=None, lse=None, scale=None, causal=False, stream=None):
+    """fa_fwd with ALiBi biases -slopes[h] * |i - j| on the scaled scores.
+    q, k, v: bfloat16 [B, H, N, d]; slopes: float32 device tensor [H].  Returns (o, lse)."""
+    B, H, N, d = _bf16_square(q, k, v)
+    if slopes.dtype != torch.float32 or tuple(slopes.shape) != (H,) or slopes.device.type != "cuda":
+        raise ValueError("slopes must be a float32 device tensor [H]")
+    slopes = slopes.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = _lib.load().fa_fwd_alibi(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  slopes.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), _lib.FA_BF16,
+                                  _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_alibi")
+    return o, lse
+
+
+def fa_fwd_blocksparse(q, k, v, block_mask, o=None, lse=None, scale=None, causal=False, stream=None):
+    """fa_fwd restricted to the allowed 128 x 128 blocks of block_mask, a uint8 (or
+    bool) device tensor [B, H, nb, nb], [H, nb, nb] or [nb, nb] with nb = ceil(N / 128);
+    missing leading dimensions are shared.  Returns (o, lse)."""
+    B, H, N, d = _bf16_square(q, k, v)
+    nb = (N + 127) // 128
+    m = block_mask
+    if m.dtype == torch.bool:
+        m = m.to(torch.uint8)
+    if m.dtype != torch.uint8 or m.device.type != "cuda" or tuple(m.shape[-2:]) != (nb, nb) or m.dim() > 4:
+        raise ValueError(f"block_mask must be a uint8 device tensor [..., {nb}, {nb}]")
+    m = m.contiguous()
+    sb = nb * nb * m.shape[-3] if m.dim() == 4 else 0
+    sh = nb * nb if m.dim() >= 3 else 0
+    if m.dim() >= 3 and m.shape[-3] != H or m.dim() == 4 and m.shape[0] != B:
+        raise ValueError("block_mask leading dimensions must be [B, H] or [H]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = _lib.load().fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                        m.data_ptr(), sb, sh, B, H, N, d, float(scale), int(bool(causal)),
+                                        _lib.FA_BF16, _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_blocksparse")
+    return o, lse
+
+
 def fa_bwd_workspace_size(B, H, N):
     """Bytes of workspace fa_bwd needs (no GPU needed)."""
     n = ctypes.c_int64()

@@ -62,11 +62,11 @@ Tile lookup_tile(int mode, int d) {
   }
 }
 
-template <int MODE, int D, bool CAUSAL>
+template <int MODE, int D, bool CAUSAL, int VAR = fa::VAR_NONE>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
   using C = Cfg<MODE, D>;
   constexpr int BC = C::BC, NW = C::NW;
-  void (*kern)(Params) = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP>;
+  void (*kern)(Params) = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR>;
   Params args = p;
   if constexpr (CAUSAL) {
     static std::atomic<int> cache[kMaxDevices];   // one per kernel
@@ -84,6 +84,22 @@ hipError_t dispatch_d(const Params& p, int d, bool causal, int grid, hipStream_t
   if (d == 128) return causal ? launch<MODE, 128, true>(p, grid, s) : launch<MODE, 128, false>(p, grid, s);
   return causal ? launch<MODE, 256, true>(p, grid, s) : launch<MODE, 256, false>(p, grid, s);
 }
+
+// ALiBi and block-sparse variants: bf16 at d = 64 and 128
+template <int VAR>
+hipError_t dispatch_variant(const Params& p, int d, bool causal, int grid, hipStream_t s) {
+  if (d == 64)
+    return causal ? launch<fa::MODE_BF16, 64, true, VAR>(p, grid, s) : launch<fa::MODE_BF16, 64, false, VAR>(p, grid, s);
+  return causal ? launch<fa::MODE_BF16, 128, true, VAR>(p, grid, s) : launch<fa::MODE_BF16, 128, false, VAR>(p, grid, s);
+}
+
+// What a variant entry point adds to the plain forward.
+struct Variant {
+  int kind = fa::VAR_NONE;
+  const float* slopes = nullptr;     // ALiBi
+  const uint8_t* bmask = nullptr;    // block-sparse
+  int64_t sb = 0, sh = 0;
+};
 
 int mode_of(int dtype) {
   return dtype == FA_BF16 ? fa::MODE_BF16 : dtype == FA_FP8_E4M3 ? fa::MODE_FP8 : fa::MODE_F32;
@@ -106,11 +122,16 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
 
 fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
               int64_t H_kv, int64_t N, int64_t d, float scale, float dq, float dk, float dv, int causal,
-              int dtype, void* stream) {
+              int dtype, void* stream, const Variant& var = Variant{}) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (var.kind == fa::VAR_ALIBI && !var.slopes) return FA_ERR_NULL;
+  if (var.kind == fa::VAR_BLOCKSPARSE && !var.bmask) return FA_ERR_NULL;
   fa_status st = check_shape(B, H, N, d, dtype);
   if (st == FA_OK && (H_kv < 1 || H % H_kv != 0)) st = FA_ERR_SHAPE;
+  if (st == FA_OK && var.kind != fa::VAR_NONE && (dtype != FA_BF16 || (d != 64 && d != 128))) st = FA_ERR_UNSUPPORTED;
+  if (st == FA_OK && var.kind == fa::VAR_BLOCKSPARSE && (var.sb < 0 || var.sh < 0)) st = FA_ERR_SHAPE;
   if (st != FA_OK) return st;
+  if (var.kind == fa::VAR_ALIBI && (reinterpret_cast<uintptr_t>(var.slopes) & 3u)) return FA_ERR_ALIGN;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_ALIGN;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   if (!(std::isfinite(dq) && dq > 0.f && std::isfinite(dk) && dk > 0.f && std::isfinite(dv) && dv > 0.f))
@@ -136,9 +157,25 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   p.qsign = 0;
   if (scale < 0.f) p.qsign = mode == fa::MODE_BF16 ? 0x80008000u : mode == fa::MODE_FP8 ? 0x80808080u : 1u;
 
+  p.H = (int)H;
+  p.slopes = var.slopes;
+  p.alibi_mul = -1.4426950408889634f / p.c2;     // c2 * alibi_mul = -log2(e)
+  p.bmask = var.bmask;
+  p.bm_sb = var.sb;
+  p.bm_sh = var.sh;
+  p.nb = (int)((N + fa::kMaskBlock - 1) / fa::kMaskBlock);
+
   const int grid = p.nrb * p.BH;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (var.kind == fa::VAR_ALIBI) {
+    e = dispatch_variant<fa::VAR_ALIBI>(p, (int)d, causal != 0, grid, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  if (var.kind == fa::VAR_BLOCKSPARSE) {
+    e = dispatch_variant<fa::VAR_BLOCKSPARSE>(p, (int)d, causal != 0, grid, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
   switch (mode) {
     case fa::MODE_BF16: e = dispatch_d<fa::MODE_BF16>(p, (int)d, causal != 0, grid, s); break;
     case fa::MODE_FP8: e = dispatch_d<fa::MODE_FP8>(p, (int)d, causal != 0, grid, s); break;
@@ -173,6 +210,25 @@ fa_status fa_fwd_gqa_fp8(const void* q8, const void* k8, const void* v8, void* o
                          float k_descale, float v_descale, int causal, void* stream) {
   return run(q8, k8, v8, o_bf16, lse, B, H, H_kv, N, d, scale, q_descale, k_descale, v_descale, causal,
              FA_FP8_E4M3, stream);
+}
+
+fa_status fa_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, const float* slopes,
+                       int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  Variant var;
+  var.kind = fa::VAR_ALIBI;
+  var.slopes = slopes;
+  return run(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream, var);
+}
+
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h, int64_t B,
+                             int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype, void* stream) {
+  Variant var;
+  var.kind = fa::VAR_BLOCKSPARSE;
+  var.bmask = block_mask;
+  var.sb = mask_stride_b;
+  var.sh = mask_stride_h;
+  return run(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream, var);
 }
 
 fa_status fa_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int dtype, int* block_rows,

@@ -27,7 +27,17 @@ struct Params {
   float c2;        // |scale| * descale_q * descale_k * log2(e)
   float out_mul;   // factor applied to O before dividing by l (fp8: descale_v / 256)
   uint32_t qsign;  // XOR mask on Q's sign bits (negative scale)
+  // variants (VAR_ALIBI, VAR_BLOCKSPARSE); unused otherwise
+  int H;                   // query heads per batch (head index = bh % H)
+  const float* slopes;     // ALiBi: [H] slopes
+  float alibi_mul;         // ALiBi: -1 / |scale| (the bias is added to the unscaled score)
+  const uint8_t* bmask;    // block-sparse: mask bytes, nonzero = block computed
+  int64_t bm_sb, bm_sh;    // block-sparse: strides of batch and head, in bytes (0 broadcasts)
+  int nb;                  // block-sparse: blocks per side, ceil(N / kMaskBlock)
 };
+
+enum { VAR_NONE = 0, VAR_ALIBI = 1, VAR_BLOCKSPARSE = 2 };
+constexpr int kMaskBlock = 128;   // block-sparse mask granularity (queries x keys)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

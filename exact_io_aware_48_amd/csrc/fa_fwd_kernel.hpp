@@ -40,6 +40,15 @@
 //     (workgroups are dealt to the 8 XCDs round-robin), keeping that head's
 //     K/V stream in one L2.
 //
+// Variants (bf16, PP off):
+//   VAR_ALIBI       : the score of query i and key j gets -slope_h * |i - j|
+//                     after scaling (added to the unscaled score as
+//                     -slope_h / |scale| * |i - j| before the softmax).
+//   VAR_BLOCKSPARSE : a byte mask over 128 x 128 (query block, key block)
+//                     pairs; the workgroup walks only the key tiles some
+//                     wave's block allows (the others are never loaded), and
+//                     each wave skips the tiles its own block does not allow.
+//
 // Numeric modes:
 //   MODE_BF16 : bf16 in/out, v_mfma_f32_32x32x16_bf16 for both products.
 //   MODE_FP8  : OCP e4m3fn in (per-tensor descales), bf16 out,
@@ -54,9 +63,12 @@
 namespace fa {
 
 // ---------------------------------------------------------------- the kernel
-template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false>
+template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false, int VAR = VAR_NONE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(Params p) {
+  static_assert(VAR == VAR_NONE || (MODE == MODE_BF16 && !PP), "variants: bf16, no ping-pong");
+  static_assert(VAR != VAR_BLOCKSPARSE || ((32 * NW) % kMaskBlock == 0 && kMaskBlock % BC == 0),
+                "row blocks and key tiles nest in the mask blocks");
   using G = Geo<D, BC, NW, MODE, PP>;
   using T = Tile<D, BC, NW, MODE>;
   constexpr int NDB = T::NDB;
@@ -157,11 +169,16 @@ void fa_fwd_kernel(Params p) {
   const int last_key = (CAUSAL ? min(N - 1, my_q) : N - 1) - 4 * ln.hf;
   typename T::PFrag pf;      // P of the current tile
 
+  // ALiBi: this head's -slope / |scale|
+  float alibi_a = 0.f;
+  if constexpr (VAR == VAR_ALIBI) alibi_a = p.slopes[bh % p.H] * p.alibi_mul;
+
   // S_j = K_j Q^T, online-softmax update, P_j packed into pf
   auto qk_softmax = [&](int j, const char FA_LDS* kbase) __attribute__((always_inline)) {
     f32x16 st[T::KB];
     T::qk(st, kbase, q, ln);
     const int key0 = j * BC;
+    if constexpr (VAR == VAR_ALIBI) T::alibi(st, (float)(my_q - key0 - 4 * ln.hf), alibi_a);
     if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0)) T::mask(st, last_key - key0);
     typename T::Softmax sm;
     T::template softmax_slices<0, T::NMAX + 1>(st, sm, m_run, c2, pf);
@@ -176,48 +193,88 @@ void fa_fwd_kernel(Params p) {
   };
   auto pv = [&](const char FA_LDS* vbase) __attribute__((always_inline)) { T::pv(oacc, vbase, pf, ln); };
 
-  // ---------------- main loop: one barrier per tile; tile j+1 is in flight
-  // while tile j is used.  The slots refilled in step j held K_{j-1} and
-  // V_{j-1} (V_{j-2} with ping-pong), whose last readers finished before the
-  // barrier that ended step j-1.
-  if constexpr (DMA) {
-    issue_tile(0, kslot(0), vslot(0));
-    wait_vmcnt<0>();
-  } else {
-    load_tile(0);
-    store_tile(kslot(0), vslot(0));
-  }
-  __syncthreads();
-
-  int ks_cur = 0, vs_cur = 0, vs_prev = G::VST - 1;  // ring slots of tile j (K, V) and of V_{j-1}
-  for (int j = 0; j < n_tiles; ++j) {
-    const int ks_next = ks_cur ^ 1;
-    const int vs_next = vs_cur + 1 == G::VST ? 0 : vs_cur + 1;
-    const bool more = j + 1 < n_tiles;
-    if (more) {                       // start fetching tile j+1 into the free slots
-      if constexpr (DMA) issue_tile(j + 1, kslot(ks_next), vslot(vs_next));
-      else load_tile(j + 1);
-    }
-    if (late) {                       // [P V_{j-1}] [S_j, softmax_j]
-      if (j >= 1 && j - 1 < wave_tiles) pv(vslot(vs_prev));
-      if (j < wave_tiles) qk_softmax(j, kslot(ks_cur));
-    } else {                          // [S_j, softmax_j] [P V_j]
-      if (j < wave_tiles) {
-        qk_softmax(j, kslot(ks_cur));
-        pv(vslot(vs_cur));
-      }
-    }
-    if constexpr (DMA) {
-      wait_vmcnt<0>();                // tile j+1 has landed
-    } else {
-      if (more) store_tile(kslot(ks_next), vslot(vs_next));
+  if constexpr (VAR == VAR_BLOCKSPARSE) {
+    // ---------------- block-sparse: only the tiles some wave's block allows
+    const uint8_t* mrow = p.bmask + (int64_t)(bh / p.H) * p.bm_sb + (int64_t)(bh % p.H) * p.bm_sh;
+    constexpr int RBLK = (32 * NW) / kMaskBlock;       // mask row blocks per workgroup
+    const int rblk0 = q_row0 / kMaskBlock;
+    const int wblk = qw0 / kMaskBlock;                 // this wave's mask row block
+    auto allows = [&](int rblk, int j) __attribute__((always_inline)) {
+      return rblk < p.nb && mrow[(int64_t)rblk * p.nb + (j * BC) / kMaskBlock] != 0;
+    };
+    auto needed = [&](int j) __attribute__((always_inline)) {
+      bool any = false;
+#pragma unroll
+      for (int r = 0; r < RBLK; ++r) any = any || allows(rblk0 + r, j);
+      return any;
+    };
+    auto next_needed = [&](int j) __attribute__((always_inline)) {
+      while (j < n_tiles && !needed(j)) ++j;
+      return j;
+    };
+    int j = next_needed(0);
+    if (j < n_tiles) {
+      issue_tile(j, kslot(0), vslot(0));
+      wait_vmcnt<0>();
     }
     __syncthreads();
-    vs_prev = vs_cur;
-    ks_cur = ks_next;
-    vs_cur = vs_next;
+    int cur = 0;
+    while (j < n_tiles) {
+      const int jn = next_needed(j + 1);
+      if (jn < n_tiles) issue_tile(jn, kslot(cur ^ 1), vslot(cur ^ 1));
+      if (j < wave_tiles && allows(wblk, j)) {
+        qk_softmax(j, kslot(cur));
+        pv(vslot(cur));
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+      cur ^= 1;
+      j = jn;
+    }
+  } else {
+    // ---------------- main loop: one barrier per tile; tile j+1 is in flight
+    // while tile j is used.  The slots refilled in step j held K_{j-1} and
+    // V_{j-1} (V_{j-2} with ping-pong), whose last readers finished before the
+    // barrier that ended step j-1.
+    if constexpr (DMA) {
+      issue_tile(0, kslot(0), vslot(0));
+      wait_vmcnt<0>();
+    } else {
+      load_tile(0);
+      store_tile(kslot(0), vslot(0));
+    }
+    __syncthreads();
+
+    int ks_cur = 0, vs_cur = 0, vs_prev = G::VST - 1;  // ring slots of tile j (K, V) and of V_{j-1}
+    for (int j = 0; j < n_tiles; ++j) {
+      const int ks_next = ks_cur ^ 1;
+      const int vs_next = vs_cur + 1 == G::VST ? 0 : vs_cur + 1;
+      const bool more = j + 1 < n_tiles;
+      if (more) {                       // start fetching tile j+1 into the free slots
+        if constexpr (DMA) issue_tile(j + 1, kslot(ks_next), vslot(vs_next));
+        else load_tile(j + 1);
+      }
+      if (late) {                       // [P V_{j-1}] [S_j, softmax_j]
+        if (j >= 1 && j - 1 < wave_tiles) pv(vslot(vs_prev));
+        if (j < wave_tiles) qk_softmax(j, kslot(ks_cur));
+      } else {                          // [S_j, softmax_j] [P V_j]
+        if (j < wave_tiles) {
+          qk_softmax(j, kslot(ks_cur));
+          pv(vslot(vs_cur));
+        }
+      }
+      if constexpr (DMA) {
+        wait_vmcnt<0>();                // tile j+1 has landed
+      } else {
+        if (more) store_tile(kslot(ks_next), vslot(vs_next));
+      }
+      __syncthreads();
+      vs_prev = vs_cur;
+      ks_cur = ks_next;
+      vs_cur = vs_next;
+    }
+    if (late && wave_tiles == n_tiles) pv(vslot(vs_prev));   // the late group's last P V
   }
-  if (late && wave_tiles == n_tiles) pv(vslot(vs_prev));   // the late group's last P V
 
   T::store(p, head_off, bh, my_q, ln, oacc, m_run, l_run);
 }

@@ -196,6 +196,16 @@ struct Tile {
         st[kb][i] = (32 * kb + 8 * (i >> 2) + (i & 3)) > lim ? -INFINITY : st[kb][i];
   }
 
+  // ALiBi: st += mul * |dq - key offset|, dq = the lane's query minus the
+  // tile's first key minus 4*hf (|i - j| is exact in fp32 below 2^24)
+  static __device__ __forceinline__ void alibi(f32x16 (&st)[KB], float dq, float mul) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        st[kb][i] = __builtin_fmaf(__builtin_fabsf(dq - (float)(32 * kb + 8 * (i >> 2) + (i & 3))), mul, st[kb][i]);
+  }
+
   // ---- the online-softmax step of one score tile, as a sequence of slices
   // (a caller may run other work between them).  In order:
   //   NMAX slices   partial maxima over 8 scores each
@@ -306,13 +316,15 @@ struct Tile {
     }
   }
 
-  // O = out_mul * O / l and L = ln2 * (m + log2 l) for query my_q
+  // O = out_mul * O / l and L = ln2 * (m + log2 l) for query my_q (a row
+  // that saw no key, possible only under a block-sparse mask: O = 0, L = -inf)
   static __device__ __forceinline__ void store(const Params& p, int64_t head_off, int bh, int my_q, const Lane& ln,
                                                const f32x16 (&oacc)[NDB], float m_run, float l_run) {
     const float l_tot = swap_halves_sum(l_run);
-    const float inv = p.out_mul / l_tot;
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? p.out_mul / l_tot : 0.f;
     if (my_q >= p.N) return;
-    if (ln.hf == 0) p.lse[(int64_t)bh * p.N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    if (ln.hf == 0) p.lse[(int64_t)bh * p.N + my_q] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

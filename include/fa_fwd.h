@@ -120,6 +120,40 @@ fa_status fa_fwd_gqa_fp8(const void* q8, const void* k8, const void* v8, void* o
                          int causal, void* stream);
 
 /*
+ * fa_fwd_alibi -- fa_fwd with ALiBi linear biases: the score of query i and
+ * key j of head h is scale * q_i . k_j - slopes[h] * |i - j| (under the
+ * causal mask, -slopes[h] * (i - j)).  The robocikowo.com "Flash Attention"
+ * page says such masks need kernel variants; the bias form is the usual
+ * ALiBi one.
+ *   slopes : device float32 [H], finite, 4-byte aligned (FA_ERR_ALIGN), not NULL
+ *   dtype  : FA_BF16 and d in {64, 128}, else FA_ERR_UNSUPPORTED
+ * Otherwise as fa_fwd.
+ */
+fa_status fa_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, const float* slopes,
+                       int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+                       void* stream);
+
+/*
+ * fa_fwd_blocksparse -- fa_fwd restricted to the allowed blocks of a block
+ * mask: the scores of query block I and key block J (128 x 128 elements,
+ * the last blocks ragged) are computed only if
+ *     block_mask[b * mask_stride_b + h * mask_stride_h + I * nb + J] != 0,
+ * nb = ceil(N / 128), and are -inf otherwise; the causal mask applies on top.
+ * Disallowed blocks are never loaded.  A row with no allowed key gets O = 0
+ * and lse = -inf.  (The pages name block-sparse patterns among the masks that
+ * need kernel variants, and FlashMask in their literature.)
+ *   block_mask    : device bytes, nb x nb per (batch, head), not NULL
+ *   mask_stride_b : bytes between batches' masks (0: one mask for all batches), >= 0
+ *   mask_stride_h : bytes between heads' masks (0: one mask for all heads), >= 0
+ *   dtype         : FA_BF16 and d in {64, 128}, else FA_ERR_UNSUPPORTED
+ * Otherwise as fa_fwd.
+ */
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
+                             void* stream);
+
+/*
  * fa_plan -- the launch fa_fwd / fa_fwd_fp8 (and their grouped-query
  * forms, whose grid does not depend on H_kv) would make for this problem,
  * without launching anything.  Any output pointer may be NULL.

@@ -31,8 +31,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_fp8", "fa_fwd_gqa",
-                                    "fa_fwd_gqa_fp8", "fa_fwd_split", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
+    assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_alibi",
+                                    "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
                                     "fa_status_string", "fa_version"]
 
 
@@ -203,3 +203,27 @@ def test_fa_fwd_split_validation(lib, kw, expected):
 ])
 def test_fa_lse_merge_validation(lib, args, expected):
     assert lib.fa_lse_merge(*args, None) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"slopes": 0}, 1), ({"q": 0}, 1), ({"dtype": 0}, 3), ({"dtype": 2}, 3), ({"d": 256}, 3), ({"N": 0}, 2),
+    ({"slopes": FAKE + 2}, 4), ({"scale": float("inf")}, 5),
+])
+def test_fa_fwd_alibi_validation(lib, kw, expected):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, slopes=FAKE, B=1, H=2, N=64, d=64, scale=0.1, causal=0, dtype=1)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "slopes", "B", "H", "N", "d", "scale", "causal", "dtype")]
+    assert lib.fa_fwd_alibi(*args, None) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"mask": 0}, 1), ({"o": 0}, 1), ({"sb": -1}, 2), ({"sh": -5}, 2), ({"dtype": 0}, 3), ({"d": 256}, 3),
+    ({"q": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
+])
+def test_fa_fwd_blocksparse_validation(lib, kw, expected):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, mask=FAKE + 1, sb=0, sh=0, B=1, H=2, N=64, d=64, scale=0.1,
+             causal=0, dtype=1)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "mask", "sb", "sh", "B", "H", "N", "d", "scale", "causal",
+                           "dtype")]
+    assert lib.fa_fwd_blocksparse(*args, None) == expected

@@ -1,0 +1,145 @@
+"""GPU parity of the ALiBi and block-sparse forward variants (fa_fwd_alibi,
+fa_fwd_blocksparse through the C ABI) against the float64 oracle
+(oracle/masks.py), element by element, at the forward's bf16 tolerances.
+Rows that see no key (block-sparse) must come back as O = 0, lse = -inf
+exactly."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_alibi, attention_blocksparse, errors
+from workloads import by_name, make_inputs
+
+from gpu_util import check, to_device
+
+pytestmark = pytest.mark.gpu
+BASE = "gpt2s_causal_bf16_b8h12n1024d64"
+
+
+def _print_case(*a):
+    print("CASE masks", *a, flush=True)
+
+
+def alibi_slopes(H):
+    """The geometric slopes 2^(-8 (h + 1) / H) of the ALiBi paper."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
+
+
+def run_alibi(x, slopes, scale=None):
+    import exact_io_aware_48_amd as fa
+    w = x.workload
+    q, k, v = to_device(x)
+    o, lse = fa.fa_fwd_alibi(q, k, v, torch.from_numpy(slopes).cuda(), scale=w.softmax_scale if scale is None
+                             else scale, causal=w.causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def run_sparse(x, bm):
+    import exact_io_aware_48_amd as fa
+    w = x.workload
+    q, k, v = to_device(x)
+    o, lse = fa.fa_fwd_blocksparse(q, k, v, torch.from_numpy(bm).cuda(), scale=w.softmax_scale, causal=w.causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_with_empty_rows(o, l, o_ref, l_ref, what):
+    empty = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l), empty), f"{what}: rows with no visible key differ"
+    assert np.all(o[empty] == 0), f"{what}: O of rows with no visible key is not 0"
+    seen = ~empty
+    if seen.any():
+        check(errors(o[seen], o_ref[seen], l[seen], l_ref[seen]), "bf16", what)
+
+
+ALIBI_CASES = [(B, H, N, d, c) for (B, H, N) in ((1, 4, 333), (2, 2, 1000), (1, 2, 1)) for d in (64, 128)
+               for c in (False, True)]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", ALIBI_CASES)
+def test_alibi_all_elements(B, H, N, d, causal):
+    _print_case("alibi", B, H, N, d, causal)
+    w = by_name(BASE).with_(B=B, H=H, N=N, d=d, causal=causal, seed=300 + N + d)
+    x = make_inputs(w)
+    slopes = alibi_slopes(H)
+    o, l = run_alibi(x, slopes)
+    o_ref, l_ref = attention_alibi(x.f64("q"), x.f64("k"), x.f64("v"), w.softmax_scale, causal,
+                                   slopes.astype(np.float64))
+    check(errors(o, o_ref, l, l_ref), "bf16", f"alibi B={B} H={H} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("scale,slopes", [(-0.1, (0.5, 0.02)), (0.3, (4.0, 0.0)), (0.0, (0.1, 1.0))])
+def test_alibi_scales_and_slopes(scale, slopes):
+    _print_case("alibi-scale", scale, slopes)
+    w = by_name(BASE).with_(B=1, H=2, N=300, d=128, causal=True, seed=44)
+    x = make_inputs(w)
+    sl = np.array(slopes, dtype=np.float32)
+    o, l = run_alibi(x, sl, scale)
+    o_ref, l_ref = attention_alibi(x.f64("q"), x.f64("k"), x.f64("v"), scale, True, sl.astype(np.float64))
+    check(errors(o, o_ref, l, l_ref), "bf16", f"alibi scale={scale} slopes={slopes}")
+
+
+def test_alibi_full_gpt2s_shape():
+    w = by_name(BASE)
+    _print_case("alibi-full", w.name)
+    x = make_inputs(w)
+    slopes = alibi_slopes(w.H)
+    o, l = run_alibi(x, slopes)
+    o_ref, l_ref = attention_alibi(x.f64("q"), x.f64("k"), x.f64("v"), w.softmax_scale, True,
+                                   slopes.astype(np.float64))
+    check(errors(o, o_ref, l, l_ref), "bf16", "alibi gpt2s")
+
+
+def _patterns(B, H, nb, seed):
+    rng = np.random.default_rng(seed)
+    local = np.zeros((nb, nb), dtype=np.uint8)
+    for i in range(nb):
+        local[i, max(0, i - 1):i + 2] = 1
+        local[i, 0] = 1                       # a global first block
+    empty_row = rng.integers(0, 2, (nb, nb)).astype(np.uint8)
+    empty_row[nb // 2] = 0                    # a row block that sees nothing
+    return {
+        "random": rng.integers(0, 2, (B, H, nb, nb)).astype(np.uint8),
+        "local_global": np.broadcast_to(local, (B, H, nb, nb)).copy(),
+        "empty_row": np.broadcast_to(empty_row, (B, H, nb, nb)).copy(),
+        "all": np.ones((B, H, nb, nb), dtype=np.uint8),
+        "none": np.zeros((B, H, nb, nb), dtype=np.uint8),
+    }
+
+
+SPARSE_CASES = [(B, H, N, d, c, pat) for (B, H, N) in ((1, 2, 700), (2, 2, 300)) for d in (64, 128)
+                for c in (False, True) for pat in ("random", "local_global", "empty_row")]
+SPARSE_CASES += [(1, 2, 513, 128, True, "all"), (1, 2, 200, 64, False, "none"), (1, 1, 1, 64, True, "all")]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,pattern", SPARSE_CASES)
+def test_blocksparse_all_elements(B, H, N, d, causal, pattern):
+    _print_case("sparse", B, H, N, d, causal, pattern)
+    w = by_name(BASE).with_(B=B, H=H, N=N, d=d, causal=causal, seed=400 + N + d)
+    x = make_inputs(w)
+    nb = (N + 127) // 128
+    bm = _patterns(B, H, nb, seed=N + d + (1 if causal else 0))[pattern]
+    o, l = run_sparse(x, bm)
+    o_ref, l_ref = attention_blocksparse(x.f64("q"), x.f64("k"), x.f64("v"), w.softmax_scale, causal, bm)
+    check_with_empty_rows(o, l, o_ref, l_ref, f"sparse B={B} H={H} N={N} d={d} causal={causal} {pattern}")
+
+
+def test_blocksparse_shared_masks():
+    """A [H, nb, nb] mask shared by the batch and an [nb, nb] mask shared by all heads."""
+    import exact_io_aware_48_amd as fa
+    _print_case("sparse-shared")
+    w = by_name(BASE).with_(B=2, H=3, N=400, d=64, causal=False, seed=9)
+    x = make_inputs(w)
+    q, k, v = to_device(x)
+    nb = 4
+    rng = np.random.default_rng(5)
+    for shape in ((3, nb, nb), (nb, nb)):
+        bm = rng.integers(0, 2, shape).astype(np.uint8)
+        o, l = fa.fa_fwd_blocksparse(q, k, v, torch.from_numpy(bm).cuda(), scale=w.softmax_scale, causal=False)
+        torch.cuda.synchronize()
+        full = np.broadcast_to(bm, (2, 3, nb, nb))
+        o_ref, l_ref = attention_blocksparse(x.f64("q"), x.f64("k"), x.f64("v"), w.softmax_scale, False, full)
+        check_with_empty_rows(o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
+                              o_ref, l_ref, f"shared mask {shape}")
