@@ -7,14 +7,17 @@ softmax, masking, normalisation, O and logsumexp stores) runs in that one
 kernel launch.  Inputs are seeded synthetic tensors (``workloads``) made
 resident in HBM before the timed region.
 
-The K timed steps are K launches of the entry point, bracketed by device
-synchronisation (``--graph``: captured once into a HIP graph and replayed).
+The K timed steps are K back-to-back launches of the entry point, bracketed by
+device synchronisation and one HIP event pair on the launch stream
+(``--graph``: captured once into a HIP graph and replayed).
 
 Prints one JSON line.  ``value`` is whole-job throughput in TFLOP/s by the
 convention 4*B*H*N^2*d (halved for the causal mask) over the K timed steps on
 the host clock.  ``roofline.achieved`` is the same FLOP count per launch over
-the kernel's mean duration from HIP events on the launch stream around every
-launch (around the replay with ``--graph``, divided by K).  ``traffic`` is the HBM bytes per launch measured with
+the mean launch duration from the HIP event pair around the timed region
+(divided by K; it includes whatever gap the GPU leaves between launches).
+``kernel_ms_p10_p50_p90`` comes from a separate untimed pass with an event pair
+around each launch, which itself adds dispatch latency.  ``traffic`` is the HBM bytes per launch measured with
 rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same
 counters give for a plain copy of known size), read from profiles/ and only
 when the kernel sources are unchanged since that measurement.
@@ -254,23 +257,36 @@ def time_launch(launch, steps, warmup, settle_s=0.25, graph=False):
         per = a.elapsed_time(b) / steps
         return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_mean": per, "kernel_ms_median": per,
                 "kernel_ms_p10": None, "kernel_ms_p90": None, "timing": f"one HIP graph replay of {steps} launches"}
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # the timed region: exactly `steps` back-to-back launches, one event pair on
+    # the launch stream around them and the host clock outside
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         launch()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = a.elapsed_time(b) / steps
+    # untimed: the spread of single launches, each bracketed by its own event pair
+    # (the pairs add dispatch latency between launches, so they time only the spread)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(min(steps, 50))]
+    for x, y in ev:
+        x.record(stream)
+        launch()
+        y.record(stream)
+    torch.cuda.synchronize()
+    kms = sorted(x.elapsed_time(y) for x, y in ev)
     return {
         "wall_ms_per_step": (t1 - t0) * 1e3 / steps,
-        "kernel_ms_mean": sum(kms) / len(kms),
+        "kernel_ms_mean": mean,
         "kernel_ms_median": kms[len(kms) // 2],
         "kernel_ms_p10": kms[len(kms) // 10],
         "kernel_ms_p90": kms[(9 * len(kms)) // 10],
-        "timing": "eager launches, one event pair per launch",
+        "timing": "eager back-to-back launches, one event pair around the timed region; "
+                  "p10/p50/p90 from a separate untimed pass with an event pair around each launch",
     }
 
 
