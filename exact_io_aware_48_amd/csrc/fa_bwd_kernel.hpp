@@ -492,7 +492,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int key0 = j * BC;
     const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0);
     const int lim = last_key - key0;
-    i32x4 dsp[2 * KB];
+    // per 32-key block: S^T, dP^T, dS^T, then that block's share of dQ^T
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 s{}, dp{};
@@ -501,23 +501,28 @@ void fa_bwd_dq_kernel(BwdParams p) {
         s = mfma_bf16(row_operand<D>(ks, kb, c, ln), qf[c], s);
         dp = mfma_bf16(row_operand<D>(vs, kb, c, ln), of[c], dp);
       }
-      float ds[16];
+      float pr[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2));
-        if (need_mask) x = (32 * kb + 8 * (i >> 2) + (i & 3)) > lim ? 0.f : x;
-        ds[i] = x * (dp[i] - dd);
+      for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2));
+      if (need_mask) {
+        asm volatile("" ::: "memory");                 // keep this a branch: only diagonal and ragged tiles mask
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pr[i] = (32 * kb + 8 * (i >> 2) + (i & 3)) > lim ? 0.f : pr[i];
       }
+      i32x4 dsp[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) dsp[2 * kb + u][w] = (int)pack_bf16x2(ds[8 * u + 2 * w], ds[8 * u + 2 * w + 1]);
+        for (int w = 0; w < 4; ++w) {
+          const int i0 = 8 * u + 2 * w;
+          dsp[u][w] = (int)pack_bf16x2(pr[i0] * (dp[i0] - dd), pr[i0 + 1] * (dp[i0 + 1] - dd));
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          dq[db] = mfma_bf16(tr_operand<D>(ks, 2 * kb + u, db, ln), __builtin_bit_cast(bf16x8, dsp[u]), dq[db]);
     }
-#pragma unroll
-    for (int s = 0; s < 2 * KB; ++s)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dq[db] = mfma_bf16(tr_operand<D>(ks, s, db, ln), __builtin_bit_cast(bf16x8, dsp[s]), dq[db]);
   };
 
   issue(0, slot(0));
