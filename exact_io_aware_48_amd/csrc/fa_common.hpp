@@ -188,13 +188,13 @@ __device__ __forceinline__ void split8(const float* x, i32x4& hi, i32x4& lo) {
 //     xcd + 8*j, and the XCD-local query head hl is query head G*(xcd + 8*(hl/G)) + hl%G.
 //   * causal: row blocks differ in work (row block i has i+1 key tiles of
 //     B_r), so the XCD's work list is ordered heaviest first.  When the whole
-//     grid is resident at once (zigzag), consecutive rounds of C slots take
+//     grid is resident at once (zigzag), consecutive passes of C slots take
 //     that list forward, backward, forward ... so every CU's workgroups add up
 //     to about the same number of tiles; otherwise heaviest-first order lets
 //     CUs that free up early take the next-heaviest block.
 __device__ __forceinline__ int zigzag_slot(int s, int total, int C) {
   const int r = s / C, pos = s - r * C, base = r * C;
-  const int R = min(C, total - base);          // slots in this round
+  const int R = min(C, total - base);          // slots in this pass
   return base + ((r & 1) ? R - 1 - pos : pos);
 }
 // P: any parameter block with the fields BH, nrb, G, xcd_heads, zigzag and cus_per_xcd.
