@@ -141,7 +141,7 @@ def backward_inputs(w):
     dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.kv_heads, w.N, w.d), dtype=torch.uint8, device="cuda")
     return q, k, v, o, lse, do, dq, dk, dv, ws
 
 

@@ -225,10 +225,10 @@ def fa_fwd_blocksparse(q, k, v, block_mask, o=None, lse=None, scale=None, causal
     return o, lse
 
 
-def fa_bwd_workspace_size(B, H, N):
+def fa_bwd_workspace_size(B, H, H_kv, N, d):
     """Bytes of workspace fa_bwd needs (no GPU needed)."""
     n = ctypes.c_int64()
-    st = _lib.load().fa_bwd_workspace_size(B, H, N, ctypes.byref(n))
+    st = _lib.load().fa_bwd_workspace_size(B, H, H_kv, N, d, ctypes.byref(n))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_bwd_workspace_size")
     return n.value
@@ -241,7 +241,7 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
     q, o, do: contiguous bfloat16 [B, H, N, d]; k, v: bfloat16 [B, H_kv, N, d]
     (H_kv dividing H); lse: float32 [B, H, N] from the forward.  dq, dk, dv:
     optional float32 outputs shaped like q, k, v; workspace: optional device
-    buffer of at least fa_bwd_workspace_size(B, H, N) bytes.  Returns (dq, dk, dv).
+    buffer of at least fa_bwd_workspace_size(B, H, H_kv, N, d) bytes.  Returns (dq, dk, dv).
     """
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
         _check(t, nm)
@@ -260,7 +260,7 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
         dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     if dv is None:
         dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    need = fa_bwd_workspace_size(B, H, N)
+    need = fa_bwd_workspace_size(B, H, H_kv, N, d)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:

@@ -22,10 +22,9 @@ using fa::BwdParams;
 // Shapes per head dim.  dK/dV: NW waves of 32 keys, each holding K and the
 // two fp32 accumulators in VGPRs.  At d = 128 the main shape stages V in LDS
 // (K, V and the accumulators would not fit the 256 VGPRs of two waves per
-// SIMD) and gives a workgroup 256 keys; a causal grid of those that fills
-// fewer than two rounds of resident workgroups is dominated by its heaviest
-// (earliest) key blocks, so it takes the small shape instead: 128 keys, one
-// wave per SIMD with K and V in VGPRs.  At d = 64 V stays in VGPRs.
+// SIMD) and gives a workgroup 256 keys; the small shape (128 keys, one wave
+// per SIMD with K and V in VGPRs) serves small causal grids (launch_dkdv).
+// At d = 64 V stays in VGPRs.
 // dQ: NW waves of 32 queries, B_c-key K/V tiles.
 template <int NW_, int WPE_, bool VLDS_> struct KvShape {
   static constexpr int NW = NW_, WPE = WPE_;
@@ -45,6 +44,13 @@ template <> struct BwdCfg<128> {
 
 int64_t stat_tiles(int64_t N) { return (N + fa::kStatRows - 1) / fa::kStatRows; }
 
+// workspace: the statistics tiles, then (grouped query heads only) room for
+// dK and dV partials of up to G parts per K/V head
+int64_t stats_bytes(int64_t BH, int64_t N) { return BH * stat_tiles(N) * (2 * fa::kStatRows) * (int64_t)sizeof(float); }
+int64_t partial_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d) {
+  return H > H_kv ? 2 * B * H * N * d * (int64_t)sizeof(float) : 0;
+}
+
 // A causal grid's workgroups are dealt zig-zag over the CUs when the whole
 // grid is resident at once (see map_block).
 template <bool CAUSAL>
@@ -59,10 +65,11 @@ void set_balance(BwdParams& p, const void* kern, int threads, int grid, std::ato
 }
 
 template <int D, bool CAUSAL, class S>
-hipError_t launch_dkdv_shape(const BwdParams& base, int64_t BHkv, hipStream_t stream) {
+hipError_t launch_dkdv_shape(const BwdParams& base, int64_t BHkv, int parts, hipStream_t stream) {
   BwdParams p = base;
   constexpr int BK = 32 * S::NW;
-  p.BH = (int)BHkv;
+  p.BH = (int)(BHkv * parts);                // (K/V head, part) pairs
+  p.parts = parts;
   p.nrb = (base.N + BK - 1) / BK;
   p.G = 1;
   p.xcd_heads = p.BH % 8 == 0 ? 1 : 0;
@@ -71,22 +78,38 @@ hipError_t launch_dkdv_shape(const BwdParams& base, int64_t BHkv, hipStream_t st
   static std::atomic<int> cache[kMaxDevices];
   set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * S::NW, grid, cache);
   void* args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * S::NW), args, 0, stream);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * S::NW), args, 0, stream);
+  if (e != hipSuccess || parts == 1) return e;
+  const int64_t n4 = BHkv * base.N * D / 4;
+  const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+  void* rargs[] = {&p, const_cast<int64_t*>(&n4)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_reduce_kernel), dim3((unsigned)blocks), dim3(256),
+                         rargs, 0, stream);
 }
 
+// Shape and split of the dK/dV launch.  A grid of main-shape workgroups that
+// fills fewer than two rounds of resident workgroups (one round without the
+// causal mask, whose blocks are equal) is dominated by its heaviest blocks:
+// grouped query heads are then split over up to G workgroups per key block
+// (partials summed afterwards); with one query head per K/V head a causal
+// grid takes the small shape instead.
 template <int D, bool CAUSAL, class BIG, class SMALL>
-hipError_t launch_dkdv(const BwdParams& base, int64_t BHkv, hipStream_t stream) {
-  if constexpr (CAUSAL && !std::is_same<BIG, SMALL>::value) {
-    constexpr int BK = 32 * BIG::NW;
-    static std::atomic<int> cache[kMaxDevices];
-    const Residency r = residency(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, BIG::NW, BIG::WPE, CAUSAL,
-                                                                                        BIG::VLDS>),
-                                  64 * BIG::NW, cache);
-    const int64_t grid = (base.N + BK - 1) / BK * BHkv;
-    if (r.resident > 0 && grid < 2 * (int64_t)r.resident)
-      return launch_dkdv_shape<D, CAUSAL, SMALL>(base, BHkv, stream);
+hipError_t launch_dkdv(const BwdParams& base, int64_t BHkv, int G, hipStream_t stream) {
+  constexpr int BK = 32 * BIG::NW;
+  static std::atomic<int> cache[kMaxDevices];
+  const Residency r = residency(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, BIG::NW, BIG::WPE, CAUSAL,
+                                                                                      BIG::VLDS>),
+                                64 * BIG::NW, cache);
+  const int64_t grid = (base.N + BK - 1) / BK * BHkv;
+  const int64_t target = (CAUSAL ? 2 : 1) * (int64_t)r.resident;
+  if (r.resident > 0 && grid < target) {
+    if (G > 1) {
+      const int parts = (int)std::min<int64_t>(G, (target + grid - 1) / grid);
+      return launch_dkdv_shape<D, CAUSAL, BIG>(base, BHkv, parts, stream);
+    }
+    if constexpr (CAUSAL && !std::is_same<BIG, SMALL>::value) return launch_dkdv_shape<D, CAUSAL, SMALL>(base, BHkv, 1, stream);
   }
-  return launch_dkdv_shape<D, CAUSAL, BIG>(base, BHkv, stream);
+  return launch_dkdv_shape<D, CAUSAL, BIG>(base, BHkv, 1, stream);
 }
 
 template <int D, bool CAUSAL>
@@ -106,7 +129,7 @@ hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv,
   }
   // 2. dK, dV: one workgroup per 32*NW keys of a K/V head
   {
-    hipError_t e = launch_dkdv<D, CAUSAL, typename C::KV, typename C::KV_SMALL>(base, B * H_kv, stream);
+    hipError_t e = launch_dkdv<D, CAUSAL, typename C::KV, typename C::KV_SMALL>(base, B * H_kv, (int)(H / H_kv), stream);
     if (e != hipSuccess) return e;
   }
   // 3. dQ: one workgroup per 32*Q_NW queries of a query head
@@ -143,10 +166,11 @@ fa_status check_bwd_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t
 
 extern "C" {
 
-fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t* bytes) {
+fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int64_t* bytes) {
   if (!bytes) return FA_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1 || B > INT_MAX / H) return FA_ERR_SHAPE;
-  *bytes = B * H * stat_tiles(N) * (2 * fa::kStatRows) * (int64_t)sizeof(float);
+  const fa_status st = check_bwd_shape(B, H, H_kv, N, d, FA_BF16);
+  if (st != FA_OK) return st;
+  *bytes = stats_bytes(B * H, N) + partial_bytes(B, H, H_kv, N, d);
   return FA_OK;
 }
 
@@ -165,6 +189,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   BwdParams p{};
   p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
   p.ws = static_cast<float*>(workspace);
+  p.part_out = p.ws + stats_bytes(B * H, N) / (int64_t)sizeof(float);
+  p.parts = 1;
   p.dq = dq; p.dk = dk; p.dv = dv;
   p.N = (int)N;
   p.qg = (int)(H / H_kv);

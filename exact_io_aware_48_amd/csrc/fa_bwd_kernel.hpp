@@ -62,6 +62,12 @@ struct BwdParams {
   int T;               // 64-query statistics tiles per head (ceil(N / 64))
   float c2;            // scale * log2(e), signed
   float scale;
+  // dK/dV with the query heads of a group split over `parts` workgroups per
+  // key block: part hp takes heads hp, hp + parts, ... and writes its share
+  // of dK and dV to part_out ([2][parts][B*H_kv][N][D], dK first); a reduction
+  // sums the parts.  parts = 1 writes dk and dv directly.
+  int parts;
+  float* part_out;
 };
 
 constexpr int kStatRows = 64;   // queries per statistics tile
@@ -269,8 +275,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
 
-  int bhk, rb;
-  map_block<CAUSAL>(p, blockIdx.x, bhk, rb);
+  int vh, rb;
+  map_block<CAUSAL>(p, blockIdx.x, vh, rb);   // vh: (K/V head, part of its query heads)
+  const int bhk = vh / p.parts, hp = vh - bhk * p.parts;
   const int kblk = p.nrb - 1 - rb;          // causal: earliest key blocks (most query tiles) first
   const int N = p.N;
   const int k0 = kblk * BK, kw0 = k0 + 32 * wave;
@@ -300,12 +307,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int T = p.T;
   const int t0 = CAUSAL ? k0 / BQ : 0;      // earlier query tiles see none of these keys
   const int nt = T - t0;
-  const int n_iter = p.qg * nt;             // (query head, query tile) pairs
+  const int nh = (p.qg - hp + p.parts - 1) / p.parts;   // query heads of this part
+  const int n_iter = nh * nt;               // (query head, query tile) pairs
 
   Stager16<D, BQ, NW> stage;
   auto issue = [&](int it, char FA_LDS* dst) __attribute__((always_inline)) {
-    const int hh = it / nt, t = t0 + it - hh * nt;
-    const int64_t bhq = (int64_t)bhk * p.qg + hh;
+    const int ih = it / nt, t = t0 + it - ih * nt;
+    const int64_t bhq = (int64_t)bhk * p.qg + hp + (int64_t)ih * p.parts;
     stage.issue(static_cast<const char*>(p.q) + bhq * N * ROWB, t * BQ, N, dst, wave, lane);
     stage.issue(static_cast<const char*>(p.dout) + bhq * N * ROWB, t * BQ, N, dst + TILEB, wave, lane);
     if (wave == 0) dma16(p.ws + (bhq * T + t) * (2 * kStatRows) + 4 * (lane & 31), dst + 2 * TILEB);
@@ -337,8 +345,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
   const float c2 = p.c2;
   auto tile = [&](int it, const char FA_LDS* qs) __attribute__((always_inline)) {
-    const int hh = it / nt, t = t0 + it - hh * nt;
-    (void)hh;
+    const int ih = it / nt, t = t0 + it - ih * nt;
     const int qt0 = t * BQ;
     if (CAUSAL && qt0 + BQ - 1 < kw0) return;          // every query of the tile precedes every key of the wave
     const char FA_LDS* dos = qs + TILEB;
@@ -418,18 +425,40 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 
   const float sc = p.scale;
+  float* dk_base = p.dk;
+  float* dv_base = p.dv;
+  if (p.parts > 1) {
+    const int64_t slab = (int64_t)p.BH / p.parts * N * D;   // one part's [B*H_kv][N][D]
+    dk_base = p.part_out + hp * slab;
+    dv_base = p.part_out + (p.parts + hp) * slab;
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int key = kw0 + 16 * kb + m;
     if (key < N) {
-      float* dkp = p.dk + kv_off + (int64_t)key * D + 4 * g;
-      float* dvp = p.dv + kv_off + (int64_t)key * D + 4 * g;
+      float* dkp = dk_base + kv_off + (int64_t)key * D + 4 * g;
+      float* dvp = dv_base + kv_off + (int64_t)key * D + 4 * g;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         *reinterpret_cast<f32x4*>(dkp + 16 * db) = dk[kb][db] * sc;
         *reinterpret_cast<f32x4*>(dvp + 16 * db) = dv[kb][db];
       }
     }
+  }
+}
+
+// dk = sum of the parts' dK, dv likewise (four floats per thread)
+__global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(BwdParams p, int64_t n4) {
+  const int64_t slab4 = n4;                 // float4s per part per tensor
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.part_out);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 a = src[i], b = src[p.parts * slab4 + i];
+    for (int hp = 1; hp < p.parts; ++hp) {
+      a += src[hp * slab4 + i];
+      b += src[(p.parts + hp) * slab4 + i];
+    }
+    reinterpret_cast<f32x4*>(p.dk)[i] = a;
+    reinterpret_cast<f32x4*>(p.dv)[i] = b;
   }
 }
 

@@ -23,9 +23,10 @@
  * Memory and streams.  Every pointer is a device pointer owned by the caller;
  * the library allocates, frees and synchronises nothing and keeps no state.
  * ``workspace`` holds fa_bwd_workspace_size() bytes of per-row statistics
- * that the call writes and then reads; its contents before and after the
- * call carry no meaning for the caller.  The work is enqueued on ``stream``
- * (a hipStream_t, NULL = default) and the call returns without waiting.
+ * (and partial sums) that the call writes and then reads; its contents
+ * before and after the call carry no meaning for the caller.  The work is
+ * enqueued on ``stream`` (a hipStream_t, NULL = default) and the call
+ * returns without waiting.
  * Outputs and workspace must not overlap each other or any input.  Results
  * are bitwise reproducible for equal inputs, shape and device (no atomics).
  *
@@ -44,11 +45,14 @@ extern "C" {
 #endif
 
 /*
- * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs for B * H query
- * heads of length N (16 * B * H * ceil(N / 64) * 32).  FA_ERR_NULL if bytes is
- * NULL, FA_ERR_SHAPE for B, H or N < 1 or B * H beyond int.
+ * fa_bwd_workspace_size -- bytes of workspace fa_bwd needs: the per-row
+ * statistics, 512 * B * H * ceil(N / 64), and with grouped query heads
+ * (H_kv < H) room for partial dK and dV sums, 8 * B * H * N * d (a small
+ * causal grid splits each group's query heads over several workgroups and
+ * adds their shares afterwards).  FA_ERR_NULL if bytes is NULL; the shape
+ * checks of fa_bwd otherwise.
  */
-fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t* bytes);
+fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int64_t* bytes);
 
 /*
  * fa_bwd -- dQ, dK and dV of exact attention, recomputing P from q, k and lse.
@@ -56,7 +60,7 @@ fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t N, int64_t* bytes)
  *   o         : the forward's output O, bfloat16 [B][H][N][d]
  *   dout      : upstream gradient dO, bfloat16 [B][H][N][d]
  *   lse       : the forward's logsumexp, float32 [B][H][N]
- *   workspace : device memory of fa_bwd_workspace_size(B, H, N) bytes
+ *   workspace : device memory of fa_bwd_workspace_size(B, H, H_kv, N, d) bytes
  *   dq        : output, float32 [B][H][N][d]
  *   dk, dv    : outputs, float32 [B][H_kv][N][d] (each K/V head's sum over its group)
  *   H_kv      : K/V heads, >= 1 and dividing H (H_kv = H: one K/V head per head)

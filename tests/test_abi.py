@@ -124,12 +124,16 @@ def test_binding_fails_loudly_without_library(monkeypatch):
 
 def test_fa_bwd_workspace_size(lib):
     n = ctypes.c_int64()
-    assert lib.fa_bwd_workspace_size(2, 3, 100, ctypes.byref(n)) == 0 and n.value == 2 * 3 * 2 * 128 * 4
-    assert lib.fa_bwd_workspace_size(1, 1, 64, ctypes.byref(n)) == 0 and n.value == 512
-    assert lib.fa_bwd_workspace_size(1, 1, 65, ctypes.byref(n)) == 0 and n.value == 1024
-    assert lib.fa_bwd_workspace_size(1, 1, 64, None) == 1
-    assert lib.fa_bwd_workspace_size(0, 1, 64, ctypes.byref(n)) == 2
-    assert lib.fa_bwd_workspace_size(1, 1, 0, ctypes.byref(n)) == 2
+    assert lib.fa_bwd_workspace_size(2, 3, 3, 100, 64, ctypes.byref(n)) == 0 and n.value == 2 * 3 * 2 * 128 * 4
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 64, 128, ctypes.byref(n)) == 0 and n.value == 512
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 65, 64, ctypes.byref(n)) == 0 and n.value == 1024
+    # grouped heads: statistics plus room for dK and dV partials of every query head
+    assert lib.fa_bwd_workspace_size(1, 8, 2, 64, 128, ctypes.byref(n)) == 0 and n.value == 8 * 512 + 2 * 8 * 64 * 128 * 4
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 64, 64, None) == 1
+    assert lib.fa_bwd_workspace_size(0, 1, 1, 64, 64, ctypes.byref(n)) == 2
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 0, 64, ctypes.byref(n)) == 2
+    assert lib.fa_bwd_workspace_size(1, 8, 3, 64, 64, ctypes.byref(n)) == 2
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 64, 256, ctypes.byref(n)) == 3
 
 
 def _bwd_args(**kw):

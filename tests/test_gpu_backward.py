@@ -151,7 +151,7 @@ def test_backward_statistics_workspace(N, d):
     x = make_inputs(w)
     do = make_grad_output(w)
     o, l = _fwd_from_oracle(x)
-    nbytes = fa.fa_bwd_workspace_size(w.B, w.H, N)
+    nbytes = fa.fa_bwd_workspace_size(w.B, w.H, w.H, N, d)
     ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     run_bwd(x, do, o, l, workspace=ws)
     T = (N + 63) // 64
