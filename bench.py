@@ -23,7 +23,7 @@ counters give for a plain copy of known size), read from profiles/ and only
 when the kernel sources are unchanged since that measurement.
 
 The line also carries ``backward``: the mean time of one fa_bwd call (its
-three launches, one event pair around the call) on the long-context,
+launches back to back) on the long-context,
 grouped-query, GPT-2-small and BERT-large workloads, in TFLOP/s by the usual
 convention of 2.5 x the forward's FLOPs.
 
@@ -146,7 +146,7 @@ def backward_inputs(w):
 
 
 def time_backward(w, steps, warmup, settle_s=0.25, graph=False):
-    """Time exactly `steps` calls of fa_bwd (statistics, dK/dV and dQ launches) on workload w."""
+    """Time exactly `steps` calls of fa_bwd (dQ with the statistics, then dK/dV) on workload w."""
     import exact_io_aware_48_amd as fa
     q, k, v, o, lse, do, dq, dk, dv, ws = backward_inputs(w)
     launch = lambda: fa.fa_bwd(q, k, v, o, do, lse, scale=w.softmax_scale, causal=w.causal, dq=dq, dk=dk, dv=dv,
@@ -514,7 +514,7 @@ def main():
             bwd[name] = {"ms_per_call": round(bt["kernel_ms_mean"], 4), "tflops": round(tf, 1),
                          "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
                          "flops": "2.5 x forward (five N x N x d products)",
-                         "launches": "statistics, dK/dV, dQ"}
+                         "launches": "dQ (with the statistics), dK/dV (+ reduction for split grouped heads)"}
         line["backward"] = bwd
     if not args.no_variants:
         var = {}

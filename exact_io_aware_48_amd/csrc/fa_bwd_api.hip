@@ -117,22 +117,8 @@ hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv,
   using C = BwdCfg<D>;
   const int N = base.N;
 
-  // 1. statistics
-  {
-    BwdParams p = base;
-    p.BH = (int)(B * H);
-    void (*kern)(BwdParams) = &fa::fa_bwd_prep_kernel<D>;
-    void* args[] = {&p};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)(p.BH * p.T)), dim3(256),
-                                   args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  // 2. dK, dV: one workgroup per 32*NW keys of a K/V head
-  {
-    hipError_t e = launch_dkdv<D, CAUSAL, typename C::KV, typename C::KV_SMALL>(base, B * H_kv, (int)(H / H_kv), stream);
-    if (e != hipSuccess) return e;
-  }
-  // 3. dQ: one workgroup per 32*Q_NW queries of a query head
+  // 1. dQ, forming the statistics of its rows on the way: one workgroup per
+  //    32*Q_NW queries of a query head
   {
     BwdParams p = base;
     constexpr int BR = 32 * C::Q_NW;
@@ -145,8 +131,12 @@ hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv,
     static std::atomic<int> cache[kMaxDevices];
     set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * C::Q_NW, grid, cache);
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * C::Q_NW), args, 0, stream);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * C::Q_NW), args, 0,
+                                   stream);
+    if (e != hipSuccess) return e;
   }
+  // 2. dK, dV: one workgroup per 32*NW keys of a K/V head, reading the statistics
+  return launch_dkdv<D, CAUSAL, typename C::KV, typename C::KV_SMALL>(base, B * H_kv, (int)(H / H_kv), stream);
 }
 
 fa_status check_bwd_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int dtype) {

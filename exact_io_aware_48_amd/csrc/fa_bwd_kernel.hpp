@@ -11,10 +11,11 @@
 // the chain rule of the forward definition (systems-analysis.info
 // "FlashAttention (PL)", "Problematyka standardowego mechanizmu uwagi").
 //
-// How (three launches, no atomics, bitwise reproducible):
-//   1. prep:  D = rowsum(dO * O) and L2 = L * log2(e) per query, written to a
-//      caller workspace in 64-query tiles [L2 x 64][D x 64]; rows past N get
-//      L2 = +inf and D = 0, so their P is exactly 0 downstream.
+// How (two launches, no atomics, bitwise reproducible):
+//   1. statistics: D = rowsum(dO * O) and L2 = L * log2(e) per query, written
+//      to a caller workspace in 64-query tiles [L2 x 64][D x 64]; rows past N
+//      get L2 = +inf and D = 0, so their P is exactly 0 downstream.  The dQ
+//      kernel (3.) forms them for its own rows as it starts, and runs first.
 //   2. dK/dV: a workgroup owns 32*NW keys of one K/V head; each wave keeps its
 //      32 keys' K and V rows in VGPRs (MFMA B operands) and its dK^T, dV^T
 //      accumulators in VGPRs, and streams the Q and dO tiles of all G query
@@ -51,7 +52,7 @@ struct BwdParams {
   float* dq;           // fp32 [B][H][N][D]
   float* dk;           // fp32 [B][H_kv][N][D]
   float* dv;
-  int BH;              // heads of this launch's grid (B*H for prep and dQ, B*H_kv for dK/dV)
+  int BH;              // heads of this launch's grid (B*H for dQ, B*H_kv times the parts for dK/dV)
   int N;
   int nrb;             // row blocks per head in this launch's grid
   int G;               // grid mapping: query heads grouped per XCD (dQ: H/H_kv; dK/dV: 1)
@@ -168,39 +169,6 @@ struct UStager {
     }
   }
 };
-
-// ---------------------------------------------------------------- 1. prep
-// One workgroup of 256 threads per 64-query tile of one head; D / 8 threads
-// share a row, each summing 8 products in fp32.
-template <int D>
-__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(BwdParams p) {
-  constexpr int TPR = D / 8;          // threads per row
-  constexpr int RPI = 256 / TPR;      // rows per pass
-  const int bh = blockIdx.x / p.T, t = blockIdx.x - bh * p.T;
-  const int r = threadIdx.x / TPR, c = threadIdx.x % TPR;
-  const int64_t head = (int64_t)bh * p.N * D;
-  float* out = p.ws + ((int64_t)bh * p.T + t) * (2 * kStatRows);
-#pragma unroll
-  for (int it = 0; it < kStatRows / RPI; ++it) {
-    const int row = it * RPI + r, qi = t * kStatRows + row;
-    float acc = 0.f;
-    if (qi < p.N) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.o) + head + (int64_t)qi * D + 8 * c);
-      const i32x4 b = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.dout) + head + (int64_t)qi * D + 8 * c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = __builtin_fmaf(bf16_lo_to_f32(a[j]), bf16_lo_to_f32(b[j]), acc);
-        acc = __builtin_fmaf(bf16_hi_to_f32(a[j]), bf16_hi_to_f32(b[j]), acc);
-      }
-    }
-#pragma unroll
-    for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (c == 0) {
-      out[row] = qi < p.N ? p.lse[(int64_t)bh * p.N + qi] * kLog2e : INFINITY;
-      out[kStatRows + row] = qi < p.N ? acc : 0.f;
-    }
-  }
-}
 
 // ---------------------------------------------------------------- 2. dK / dV
 // v_mfma_f32_16x16x32_bf16 on a wave64, lane = 16*g + m:
@@ -463,6 +431,8 @@ __global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(BwdParams p, int64_t
 }
 
 // ---------------------------------------------------------------- 3. dQ
+// The dQ workgroup also forms its rows of the statistics workspace, which
+// the dK/dV launch that follows reads.
 template <int D, int BC, int NW, int WPE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fa_bwd_dq_kernel(BwdParams p) {
@@ -489,11 +459,34 @@ void fa_bwd_dq_kernel(BwdParams p) {
   bf16x8 qf[NSTEP], of[NSTEP];
   load_frag<D>(p.q, head_off, my_q, N, ln, qf);
   load_frag<D>(p.dout, head_off, my_q, N, ln, of);
-  float l2 = INFINITY, dd = 0.f;              // queries past the padded tiles: P = 0
-  if (my_q < p.T * kStatRows) {
-    const float* w = p.ws + ((int64_t)bh * p.T + my_q / kStatRows) * (2 * kStatRows) + my_q % kStatRows;
-    l2 = w[0];
-    dd = w[kStatRows];
+  // this query's statistics: D = rowsum(dO * O) (each lane half sums its
+  // half of the dims) and L2 = L * log2(e); queries past N get +inf and 0, so
+  // their P is 0.  They are also written to the workspace for the dK/dV
+  // launch that follows.
+  float l2 = INFINITY, dd = 0.f;
+  {
+    bf16x8 of_o[NSTEP];
+    load_frag<D>(p.o, head_off, my_q, N, ln, of_o);
+    float part = 0.f;
+#pragma unroll
+    for (int c = 0; c < NSTEP; ++c) {
+      const i32x4 a = __builtin_bit_cast(i32x4, of_o[c]), b = __builtin_bit_cast(i32x4, of[c]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        part = __builtin_fmaf(bf16_lo_to_f32(a[j]), bf16_lo_to_f32(b[j]), part);
+        part = __builtin_fmaf(bf16_hi_to_f32(a[j]), bf16_hi_to_f32(b[j]), part);
+      }
+    }
+    const float dsum = swap_halves_sum(part);
+    if (my_q < N) {
+      l2 = p.lse[(int64_t)bh * N + my_q] * kLog2e;
+      dd = dsum;
+    }
+    if (ln.hf == 0 && my_q < p.T * kStatRows) {
+      float* w = p.ws + ((int64_t)bh * p.T + my_q / kStatRows) * (2 * kStatRows) + my_q % kStatRows;
+      w[0] = l2;
+      w[kStatRows] = dd;
+    }
   }
 
   f32x16 dq[NDB];
