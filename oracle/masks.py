@@ -24,17 +24,20 @@ import numpy as np
 BLOCK = 128
 
 
-def attention_biased(q, k, v, scale, causal, bias=None, allowed=None):
-    """O [N, d] and L [N] of one head with an optional additive bias [N, N]
-    (added after scaling) and an optional boolean mask of allowed scores [N, N]."""
+def attention_biased(q, k, v, scale, causal, bias=None, allowed=None, rows=None):
+    """O and L of one head with an optional additive bias (added after
+    scaling) and an optional boolean mask of allowed scores.  q, k, v [N, d];
+    rows: the query rows to compute (default all); bias and allowed are
+    [len(rows), N], the rows' lines of the full N x N matrices."""
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
-    N = q.shape[0]
-    s = scale * (q @ k.T)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    N = len(rows)
+    s = scale * (q[rows] @ k.T)
     if bias is not None:
         s = s + bias
     keep = np.ones((N, k.shape[0]), dtype=bool) if allowed is None else np.asarray(allowed, dtype=bool)
     if causal:
-        keep &= np.arange(k.shape[0])[None, :] <= np.arange(N)[:, None]
+        keep &= np.arange(k.shape[0])[None, :] <= rows[:, None]
     s = np.where(keep, s, -np.inf)
     m = s.max(axis=1)
     m_safe = np.where(np.isfinite(m), m, 0.0)
@@ -48,10 +51,11 @@ def attention_biased(q, k, v, scale, causal, bias=None, allowed=None):
     return o, lse
 
 
-def alibi_bias(N, slope):
-    """-slope * |i - j| for an N x N score matrix."""
+def alibi_bias(N, slope, rows=None):
+    """-slope * |i - j| for an N x N score matrix (or its given rows)."""
     idx = np.arange(N, dtype=np.float64)
-    return -float(slope) * np.abs(idx[:, None] - idx[None, :])
+    ri = idx if rows is None else np.asarray(rows, dtype=np.float64)
+    return -float(slope) * np.abs(ri[:, None] - idx[None, :])
 
 
 def attention_alibi(q, k, v, scale, causal, slopes):
@@ -67,11 +71,12 @@ def attention_alibi(q, k, v, scale, causal, slopes):
     return o, lse
 
 
-def expand_block_mask(block_mask, N, block=BLOCK):
-    """Boolean [N, N] from a block mask [ceil(N/block), ceil(N/block)]."""
+def expand_block_mask(block_mask, N, block=BLOCK, rows=None):
+    """Boolean [N, N] (or its given rows) from a block mask [ceil(N/block), ceil(N/block)]."""
     bm = np.asarray(block_mask, dtype=bool)
     idx = np.arange(N) // block
-    return bm[idx[:, None], idx[None, :]]
+    ridx = idx if rows is None else np.asarray(rows, dtype=np.int64) // block
+    return bm[ridx[:, None], idx[None, :]]
 
 
 def attention_blocksparse(q, k, v, scale, causal, block_mask):

@@ -157,3 +157,19 @@ def _sparse_mutant(kind):
 @pytest.mark.parametrize("kind", ["transposed", "block_off_by_one"])
 def test_sparse_pins_reject_planted_mistakes(kind):
     assert not _sparse_pins_hold(_sparse_mutant(kind))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_restricted_rows_agree_with_whole_matrix(causal):
+    rng = np.random.default_rng(31)
+    N = BLOCK + 50
+    q, k, v = (rng.standard_normal((N, 5)) for _ in range(3))
+    rows = np.array([0, 3, BLOCK - 1, BLOCK, N - 1])
+    bias = alibi_bias(N, 0.3)
+    o, l = attention_biased(q, k, v, SCALE, causal, bias=bias)
+    o2, l2 = attention_biased(q, k, v, SCALE, causal, bias=alibi_bias(N, 0.3, rows), rows=rows)
+    assert np.allclose(o2, o[rows], rtol=0, atol=1e-13) and np.allclose(l2, l[rows], rtol=0, atol=1e-13)
+    bm = np.array([[1, 0], [1, 1]], dtype=np.uint8)
+    o, l = attention_biased(q, k, v, SCALE, causal, allowed=expand_block_mask(bm, N))
+    o2, l2 = attention_biased(q, k, v, SCALE, causal, allowed=expand_block_mask(bm, N, rows=rows), rows=rows)
+    assert np.allclose(o2, o[rows], rtol=0, atol=1e-13) and np.allclose(l2, l[rows], rtol=0, atol=1e-13)
