@@ -215,6 +215,15 @@ def test_backward_full_gpt2s_all_elements():
     check_grads(run_bwd(x, do, o, l), oracle_bwd(x, do), w.name)
 
 
+def test_backward_full_bertl_all_elements():
+    w = by_name("bertl_bf16_b16h16n512d64")
+    _print_case("full", w.name)
+    x = make_inputs(w)
+    do = make_grad_output(w)
+    o, l = _fwd_from_gpu(x)
+    check_grads(run_bwd(x, do, o, l), oracle_bwd(x, do), w.name)
+
+
 @pytest.mark.parametrize("name,heads", [("long_causal_bf16_b1h32n8192d128", (0, 31)),
                                         ("gqa_causal_bf16_b1h32kv8n8192d128", (5,))])
 def test_backward_full_sampled(name, heads):

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from oracle import attention_alibi, attention_blocksparse, errors
+from oracle.masks import alibi_bias, attention_biased, expand_block_mask
 from workloads import by_name, make_inputs
 
 from gpu_util import check, to_device
@@ -143,3 +144,43 @@ def test_blocksparse_shared_masks():
         o_ref, l_ref = attention_blocksparse(x.f64("q"), x.f64("k"), x.f64("v"), w.softmax_scale, False, full)
         check_with_empty_rows(o.float().cpu().numpy().astype(np.float64), l.cpu().numpy().astype(np.float64),
                               o_ref, l_ref, f"shared mask {shape}")
+
+
+def _sample_rows(N, seed):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 127, 128, 255, 256, N // 2, N - 2, N - 1]
+    return np.unique(np.concatenate([edges, rng.choice(N, 20, replace=False)]))
+
+
+def test_alibi_full_long_causal_sampled():
+    """The long-context causal workload with ALiBi, as the benchmark times it:
+    sampled rows of sampled heads."""
+    w = by_name("long_causal_bf16_b1h32n8192d128")
+    _print_case("alibi-long", w.name)
+    x = make_inputs(w)
+    slopes = alibi_slopes(w.H)
+    o, l = run_alibi(x, slopes)
+    rows = _sample_rows(w.N, 1)
+    for h in (0, 17, 31):
+        o_ref, l_ref = attention_biased(x.f64("q", 0, h), x.f64("k", 0, h), x.f64("v", 0, h), w.softmax_scale, True,
+                                        bias=alibi_bias(w.N, float(slopes[h]), rows), rows=rows)
+        check(errors(o[0, h, rows], o_ref, l[0, h, rows], l_ref), "bf16", f"alibi long head {h}")
+
+
+def test_blocksparse_full_sliding_window_sampled():
+    """N = 8192, d = 128, 32 heads, non-causal, each 128-query block seeing its
+    neighbours and the first key block (the benchmark's pattern): sampled rows."""
+    w = by_name("long_causal_bf16_b1h32n8192d128").with_(causal=False)
+    _print_case("sparse-long")
+    x = make_inputs(w)
+    nb = w.N // 128
+    bm = np.zeros((nb, nb), dtype=np.uint8)
+    for i in range(nb):
+        bm[i, max(0, i - 1):i + 2] = 1
+        bm[i, 0] = 1
+    o, l = run_sparse(x, bm)
+    rows = _sample_rows(w.N, 2)
+    for h in (0, 31):
+        o_ref, l_ref = attention_biased(x.f64("q", 0, h), x.f64("k", 0, h), x.f64("v", 0, h), w.softmax_scale, False,
+                                        allowed=expand_block_mask(bm, w.N, rows=rows), rows=rows)
+        check(errors(o[0, h, rows], o_ref, l[0, h, rows], l_ref), "bf16", f"sparse long head {h}")
