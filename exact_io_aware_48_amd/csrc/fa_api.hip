@@ -31,16 +31,21 @@ struct Tile {
 // more workgroups.  d = 256 with 16-bit tiles uses 32-key tiles to stay
 // within 256 VGPRs at two waves per SIMD.  PP: ping-pong wave groups (the
 // upper half of the waves runs P V one tile late), which pays off for fp8.
+// PRIO: raised wave priority outside the MFMA blocks (d = 256 bf16).
 template <int MODE, int D> struct Cfg;
-template <> struct Cfg<fa::MODE_BF16, 64> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
-template <> struct Cfg<fa::MODE_BF16, 128> { static constexpr int BC = 128, NW = 8; static constexpr bool PP = false; };
-template <> struct Cfg<fa::MODE_BF16, 256> { static constexpr int BC = 32, NW = 8; static constexpr bool PP = false; };
-template <> struct Cfg<fa::MODE_FP8, 64> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
-template <> struct Cfg<fa::MODE_FP8, 128> { static constexpr int BC = 64, NW = 8; static constexpr bool PP = true; };
-template <> struct Cfg<fa::MODE_FP8, 256> { static constexpr int BC = 64, NW = 8; static constexpr bool PP = true; };
-template <> struct Cfg<fa::MODE_F32, 64> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
-template <> struct Cfg<fa::MODE_F32, 128> { static constexpr int BC = 64, NW = 4; static constexpr bool PP = false; };
-template <> struct Cfg<fa::MODE_F32, 256> { static constexpr int BC = 32, NW = 4; static constexpr bool PP = false; };
+template <int BC_, int NW_, bool PP_, bool PRIO_ = false> struct Shape {
+  static constexpr int BC = BC_, NW = NW_;
+  static constexpr bool PP = PP_, PRIO = PRIO_;
+};
+template <> struct Cfg<fa::MODE_BF16, 64> : Shape<64, 4, false> {};
+template <> struct Cfg<fa::MODE_BF16, 128> : Shape<128, 8, false> {};
+template <> struct Cfg<fa::MODE_BF16, 256> : Shape<32, 8, false, true> {};
+template <> struct Cfg<fa::MODE_FP8, 64> : Shape<64, 4, false> {};
+template <> struct Cfg<fa::MODE_FP8, 128> : Shape<64, 8, true> {};
+template <> struct Cfg<fa::MODE_FP8, 256> : Shape<64, 8, true> {};
+template <> struct Cfg<fa::MODE_F32, 64> : Shape<64, 4, false> {};
+template <> struct Cfg<fa::MODE_F32, 128> : Shape<64, 4, false> {};
+template <> struct Cfg<fa::MODE_F32, 256> : Shape<32, 4, false> {};
 
 template <int MODE, int D>
 Tile tile_for() {
@@ -66,7 +71,7 @@ template <int MODE, int D, bool CAUSAL, int VAR = fa::VAR_NONE>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
   using C = Cfg<MODE, D>;
   constexpr int BC = C::BC, NW = C::NW;
-  void (*kern)(Params) = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR>;
+  void (*kern)(Params) = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR, VAR == fa::VAR_NONE && C::PRIO>;
   Params args = p;
   if constexpr (CAUSAL) {
     static std::atomic<int> cache[kMaxDevices];   // one per kernel
