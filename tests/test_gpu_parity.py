@@ -162,6 +162,27 @@ def test_large_scores_from_shifted_keys():
     check(errors(o, ref, l, lref), "bf16", "shifted keys")
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 64), ("fp8", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_max_grows_at_row_dependent_rates(dtype, d, causal):
+    """Scores rise along the keys at a different rate for every query row, so
+    the running maximum grows by more than the rescale threshold on many
+    tiles, by different amounts in neighbouring rows (the rescale of O and l
+    must use each row's own factor)."""
+    N = 400
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=2, N=N, d=d, dtype=dtype, causal=causal)
+    base = make_inputs(w.with_(dtype="f32"))
+    rate = (np.arange(N) % 7).astype(np.float32)[None, None, :, None] * np.float32(0.25)
+    ramp = (np.arange(N) / N).astype(np.float32)[None, None, :, None] * np.float32(4.0)
+    q = base.q * np.float32(0.5) + rate
+    k = base.k * np.float32(0.5) + ramp
+    x = from_f32(w, q, k, base.v)
+    _print_case("row-rates", dtype, d, causal)
+    o, l = run_gpu(x)
+    ref, lref = oracle_full(x)
+    check(errors(o, ref, l, lref), dtype, f"row-dependent growth {dtype} d={d} causal={causal}")
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
 def test_other_scales(scale):
     w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=2, N=190, d=64, causal=True)
