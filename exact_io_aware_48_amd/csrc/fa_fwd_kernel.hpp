@@ -86,7 +86,9 @@ void fa_fwd_kernel(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform in an SGPR, so that LDS and DMA addresses stay scalar (not
+  // with ping-pong, whose fp8 d = 256 instance then spills)
+  const int wave = PP ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
   const typename T::Lane ln = T::lane_info(lane);
   const bool late = PP && wave >= NW / 2;   // ping-pong: this wave runs P V one tile late
 
@@ -255,35 +257,63 @@ void fa_fwd_kernel(Params p) {
     }
     __syncthreads();
 
-    int ks_cur = 0, vs_cur = 0, vs_prev = G::VST - 1;  // ring slots of tile j (K, V) and of V_{j-1}
-    for (int j = 0; j < n_tiles; ++j) {
-      const int ks_next = ks_cur ^ 1;
-      const int vs_next = vs_cur + 1 == G::VST ? 0 : vs_cur + 1;
-      const bool more = j + 1 < n_tiles;
-      if (more) {                       // start fetching tile j+1 into the free slots
-        if constexpr (DMA) issue_tile(j + 1, kslot(ks_next), vslot(vs_next));
-        else load_tile(j + 1);
-      }
-      if (late) {                       // [P V_{j-1}] [S_j, softmax_j]
-        if (j >= 1 && j - 1 < wave_tiles) pv(vslot(vs_prev));
-        if (j < wave_tiles) qk_softmax(j, kslot(ks_cur));
-      } else {                          // [S_j, softmax_j] [P V_j]
-        if (j < wave_tiles) {
-          qk_softmax(j, kslot(ks_cur));
-          pv(vslot(vs_cur));
+    if constexpr (!PP) {
+      // two-slot ring: step j uses slot j % 2 and fills the other; unrolled
+      // by two so that the slot offsets are constants of the LDS instructions
+      auto step = [&](int j, int sl) __attribute__((always_inline)) {
+        const bool more = j + 1 < n_tiles;
+        if (more) {                     // start fetching tile j+1 into the free slots
+          if constexpr (DMA) issue_tile(j + 1, kslot(sl ^ 1), vslot(sl ^ 1));
+          else load_tile(j + 1);
         }
+        if (j < wave_tiles) {
+          qk_softmax(j, kslot(sl));
+          pv(vslot(sl));
+        }
+        if constexpr (DMA) {
+          wait_vmcnt<0>();              // tile j+1 has landed
+        } else {
+          if (more) store_tile(kslot(sl ^ 1), vslot(sl ^ 1));
+        }
+        __syncthreads();
+      };
+      int j = 0;
+      for (; j + 1 < n_tiles; j += 2) {
+        step(j, 0);
+        step(j + 1, 1);
       }
-      if constexpr (DMA) {
-        wait_vmcnt<0>();                // tile j+1 has landed
-      } else {
-        if (more) store_tile(kslot(ks_next), vslot(vs_next));
+      if (j < n_tiles) step(j, 0);
+    } else {
+      int ks_cur = 0, vs_cur = 0, vs_prev = G::VST - 1;  // ring slots of tile j (K, V) and of V_{j-1}
+      for (int j = 0; j < n_tiles; ++j) {
+        const int ks_next = ks_cur ^ 1;
+        const int vs_next = vs_cur + 1 == G::VST ? 0 : vs_cur + 1;
+        const bool more = j + 1 < n_tiles;
+        if (more) {                       // start fetching tile j+1 into the free slots
+          if constexpr (DMA) issue_tile(j + 1, kslot(ks_next), vslot(vs_next));
+          else load_tile(j + 1);
+        }
+        if (late) {                       // [P V_{j-1}] [S_j, softmax_j]
+          if (j >= 1 && j - 1 < wave_tiles) pv(vslot(vs_prev));
+          if (j < wave_tiles) qk_softmax(j, kslot(ks_cur));
+        } else {                          // [S_j, softmax_j] [P V_j]
+          if (j < wave_tiles) {
+            qk_softmax(j, kslot(ks_cur));
+            pv(vslot(vs_cur));
+          }
+        }
+        if constexpr (DMA) {
+          wait_vmcnt<0>();                // tile j+1 has landed
+        } else {
+          if (more) store_tile(kslot(ks_next), vslot(vs_next));
+        }
+        __syncthreads();
+        vs_prev = vs_cur;
+        ks_cur = ks_next;
+        vs_cur = vs_next;
       }
-      __syncthreads();
-      vs_prev = vs_cur;
-      ks_cur = ks_next;
-      vs_cur = vs_next;
+      if (late && wave_tiles == n_tiles) pv(vslot(vs_prev));   // the late group's last P V
     }
-    if (late && wave_tiles == n_tiles) pv(vslot(vs_prev));   // the late group's last P V
   }
 
   T::store(p, head_off, bh, my_q, ln, oacc, m_run, l_run);
