@@ -240,7 +240,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
   char FA_LDS* const vsm = smem + 2 * STAGEB;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index in an SGPR, so that LDS and DMA addresses stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 15, g = lane >> 4;
 
   int vh, rb;
@@ -446,7 +447,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char smem_raw[2 * STAGEB];
   char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index in an SGPR, so that LDS and DMA addresses stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BwdLane ln = bwd_lane(lane);
 
   int bh, rb;
@@ -550,14 +552,19 @@ void fa_bwd_dq_kernel(BwdParams p) {
   issue(0, slot(0));
   wait_vmcnt<0>();
   __syncthreads();
-  int cur = 0;
-  for (int j = 0; j < n_tiles; ++j) {
-    if (j + 1 < n_tiles) issue(j + 1, slot(cur ^ 1));
-    if (j < wave_tiles) tile(j, slot(cur));
+  // two-slot ring, unrolled by two so that the slot offsets are constants
+  auto step = [&](int j, int sl) __attribute__((always_inline)) {
+    if (j + 1 < n_tiles) issue(j + 1, slot(sl ^ 1));
+    if (j < wave_tiles) tile(j, slot(sl));
     wait_vmcnt<0>();
     __syncthreads();
-    cur ^= 1;
+  };
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, 0);
+    step(j + 1, 1);
   }
+  if (j < n_tiles) step(j, 0);
 
   if (my_q < N) {
     float* dst = p.dq + head_off + (int64_t)my_q * D;
