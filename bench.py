@@ -32,7 +32,11 @@ workloads (TFLOP/s by the plain convention) and a block-sparse sliding
 window with one global block (TFLOP/s over the allowed query/key pairs,
 and the speed-up over the dense kernel).  And ``decode``: one fa_fwd_split call (split kernel and merge) on
 the decode workloads, as HBM bandwidth over the compulsory bytes (K and V
-read once) against the 8 TB/s peak.
+read once) against the 8 TB/s peak.  ``cold``: the GPT-2- and BERT-shaped
+forward workloads (whose inputs fit in the 256 MiB MALL) timed with a 512 MiB
+device write before every launch, p10/p50/p90 of single launches.  ``gpu``:
+the device name, architecture and compute units, and its clocks read with
+rocm-smi (or amd-smi) right after the timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
     python bench.py --backward-only --workload NAME   time only fa_bwd on NAME (for profiling runs)
@@ -58,6 +62,8 @@ HEADLINE = "gpt2s_causal_bf16_b8h12n1024d64"
 METRIC = "attention fwd TFLOP/s and % of MI355X dense MFMA peak at N=1K–16K, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 2516.6, "fp8": 5033.2}   # dense MFMA peaks of the type the products use
 HBM_GBPS = 8000.0
+# forward workloads whose inputs fit in the 256 MiB MALL: also timed cold
+COLD_WORKLOADS = ["gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64"]
 BWD_WORKLOADS = ["long_causal_bf16_b1h32n8192d128", "gqa_causal_bf16_b1h32kv8n8192d128",
                  "gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64"]
 KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_tile.hpp",
@@ -290,6 +296,78 @@ def time_launch(launch, steps, warmup, settle_s=0.25, graph=False):
     }
 
 
+def time_cold(w, iters=30, scratch_bytes=512 * 2**20):
+    """Cold-cache series: before each launch a 512 MiB scratch write evicts the
+    L2s and the 256 MiB MALL (the GPT-2- and BERT-shaped inputs fit in the
+    MALL), then one event pair on the launch stream times the launch alone."""
+    import torch
+    import exact_io_aware_48_amd as fa
+    x, q, k, v = device_inputs(w)
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    f = fa.fa_fwd_gqa if w.kv_heads != w.H else fa.fa_fwd
+    launch = lambda: f(q, k, v, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+    scratch = torch.empty(scratch_bytes // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):                  # untimed warmup
+        scratch.fill_(0.0)
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(ev):
+        scratch.fill_(float(i))
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    kms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = kms[len(kms) // 2]
+    return {"kernel_ms_p10_p50_p90": [round(kms[len(kms) // 10], 5), round(med, 5), round(kms[(9 * len(kms)) // 10], 5)],
+            "tflops_at_median": round(w.flops / (med * 1e-3) / 1e12, 1),
+            "iterations": iters, "eviction": f"{scratch_bytes >> 20} MiB device write before each launch"}
+
+
+def gpu_info():
+    """The GPU model (from the runtime) and its clocks right after the timed
+    region (rocm-smi, else amd-smi); a tool that is missing or fails leaves
+    its error text instead."""
+    import subprocess
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1)}
+    for cmd in (["rocm-smi", "--showclocks", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired) as e:
+            info["clocks_error"] = f"{' '.join(cmd)}: {e}"
+            continue
+        if r.returncode != 0:
+            info["clocks_error"] = f"{' '.join(cmd)}: exit {r.returncode}: {(r.stderr or r.stdout).strip()[:200]}"
+            continue
+        try:
+            data = json.loads(r.stdout)
+        except ValueError:
+            info["clocks_error"] = f"{' '.join(cmd)}: output is not JSON"
+            continue
+        found = {}
+
+        def walk(node, path):
+            if isinstance(node, dict):
+                for key, val in node.items():
+                    walk(val, path + [str(key)])
+            elif isinstance(node, list):
+                for i, val in enumerate(node):
+                    walk(val, path + [str(i)])
+            elif any(t in path[-1].lower() for t in ("sclk", "mclk", "gfx")) and len(found) < 16:
+                found["/".join(path)] = node
+        walk(data, [])
+        info["clocks"] = {"tool": cmd[0], "values": found}
+        info.pop("clocks_error", None)
+        break
+    return info
+
+
 def copy_calibration(nbytes=256 * 2**20, reps=3):
     """A plain device copy of known size, so PMC byte counters can be scaled."""
     import torch
@@ -421,6 +499,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip timing the split-KV decode workloads")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the ALiBi and block-sparse variants")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache series")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only fa_bwd on --workload and print its line (for profiling runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -505,6 +584,8 @@ def main():
                                "kernel_ms_median": round(ot["kernel_ms_median"], 4), "dtype": ow.dtype,
                                "peak": opk}
         line["other_workloads"] = others
+    if not args.no_cold and not args.only_headline:
+        line["cold"] = {name: time_cold(by_name(name)) for name in COLD_WORKLOADS}
     if not args.no_backward:
         bwd = {}
         for name in BWD_WORKLOADS:
@@ -550,6 +631,7 @@ def main():
         line["decode"] = dec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
+    line["gpu"] = gpu_info()
     print(json.dumps(line), flush=True)
     return 0
 
