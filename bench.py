@@ -35,14 +35,16 @@ the decode workloads, as HBM bandwidth over the compulsory bytes (K and V
 read once) against the 8 TB/s peak.  ``cold``: the GPT-2- and BERT-shaped
 forward workloads (whose inputs fit in the 256 MiB MALL) timed with a 512 MiB
 device write before every launch, p10/p50/p90 of single launches.  ``gpu``:
-the device name, architecture and compute units, and its clocks read with
-rocm-smi (or amd-smi) right after the timed region.
+the device name, architecture and compute units, and the current clock
+levels from the driver's sysfs files right after the timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
     python bench.py --backward-only --workload NAME   time only fa_bwd on NAME (for profiling runs)
     python bench.py --copy-calibration ...     also run a 256 MiB device copy (for PMC scaling)
     python bench.py --summarize-pmc DIR_FETCH DIR_WRITE --workload NAME
                                                write profiles/traffic_<NAME>.json from two PMC runs
+    python bench.py --summarize-counters DIR... --workload NAME
+                                               write profiles/counters_<NAME>.txt from SQ counter passes
 """
 
 import argparse
@@ -328,43 +330,25 @@ def time_cold(w, iters=30, scratch_bytes=512 * 2**20):
 
 
 def gpu_info():
-    """The GPU model (from the runtime) and its clocks right after the timed
-    region (rocm-smi, else amd-smi); a tool that is missing or fails leaves
-    its error text instead."""
-    import subprocess
+    """The GPU model (from the runtime) and the current clock levels from the
+    driver's sysfs files (pp_dpm_sclk / pp_dpm_mclk of each card it exposes,
+    read right after the timed region).  Plain file reads: nothing is spawned
+    from this GPU-initialised process."""
     import torch
     pr = torch.cuda.get_device_properties(0)
     info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
             "memory_gib": round(pr.total_memory / 2**30, 1)}
-    for cmd in (["rocm-smi", "--showclocks", "--json"], ["amd-smi", "metric", "--clock", "--json"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
-        except (OSError, subprocess.TimeoutExpired) as e:
-            info["clocks_error"] = f"{' '.join(cmd)}: {e}"
-            continue
-        if r.returncode != 0:
-            info["clocks_error"] = f"{' '.join(cmd)}: exit {r.returncode}: {(r.stderr or r.stdout).strip()[:200]}"
-            continue
-        try:
-            data = json.loads(r.stdout)
-        except ValueError:
-            info["clocks_error"] = f"{' '.join(cmd)}: output is not JSON"
-            continue
-        found = {}
-
-        def walk(node, path):
-            if isinstance(node, dict):
-                for key, val in node.items():
-                    walk(val, path + [str(key)])
-            elif isinstance(node, list):
-                for i, val in enumerate(node):
-                    walk(val, path + [str(i)])
-            elif any(t in path[-1].lower() for t in ("sclk", "mclk", "gfx")) and len(found) < 16:
-                found["/".join(path)] = node
-        walk(data, [])
-        info["clocks"] = {"tool": cmd[0], "values": found}
-        info.pop("clocks_error", None)
-        break
+    clocks = {}
+    for kind in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}"))[:8]:
+            try:
+                with open(path) as f:
+                    levels = f.read().splitlines()
+            except OSError:
+                continue
+            cur = [ln.split(":", 1)[-1].replace("*", "").strip() for ln in levels if ln.rstrip().endswith("*")]
+            clocks[f"{path.split('/')[4]}/{kind}"] = cur[0] if cur else None
+    info["clocks"] = clocks if clocks else "no readable /sys/class/drm/card*/device/pp_dpm_sclk"
     return info
 
 
@@ -451,6 +435,62 @@ def summarize_pmc(dir_fetch, dir_write, workload_name, command=""):
     print(json.dumps(res))
 
 
+# per-instruction FLOPs of the MFMAs the forward issues (32x32x16 bf16, 32x32x64 fp8)
+MFMA_FLOPS = {"bf16": 2 * 32 * 32 * 16, "fp8": 2 * 32 * 32 * 64}
+SIMDS = 256 * 4
+SPEC_CLOCK_GHZ = 2.4
+
+
+def summarize_counters(dirs, workload_name, command=""):
+    """SQ counters of the forward kernel (one rocprofv3 --pmc pass per
+    directory), averaged over its dispatches, with derived ratios: instructions
+    per MFMA, LDS bank conflicts per LDS instruction, and the MFMA busy
+    fraction over all SIMDs for the kernel's mean duration in
+    profiles/kernel_trace_<workload>.txt at the 2.4 GHz spec clock."""
+    from workloads import by_name
+    w = by_name(workload_name)
+    vals = {}
+    for d in dirs:
+        for r in _read_counter_csv(d):
+            if "fa_fwd_kernel" in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no fa_fwd_kernel dispatch in {dirs}")
+    mean = {k: sum(v) / len(v) for k, v in sorted(vals.items())}
+    lines = [f"# SQ counters of the forward kernel: {workload_name}", "",
+             f"command (one pass per counter set): {command}", "",
+             "counter                          dispatches   mean per dispatch"]
+    lines += [f"{k:32s} {len(vals[k]):10d}   {mean[k]:18.1f}" for k in mean]
+    mf = mean.get("SQ_INSTS_MFMA")
+    derived = []
+    if mf:
+        for k, label in (("SQ_INSTS_VALU", "VALU instructions per MFMA (the count includes the MFMAs)"),
+                         ("SQ_INSTS_VALU_TRANS_F32", "transcendental (exp) instructions per MFMA"),
+                         ("SQ_INSTS_LDS", "LDS instructions per MFMA"),
+                         ("SQ_INSTS_SALU", "scalar instructions per MFMA")):
+            if k in mean:
+                derived.append(f"{label}: {mean[k] / mf:.2f}")
+        flops = mf * MFMA_FLOPS["fp8" if w.dtype == "fp8" else "bf16"]
+        derived.append(f"MFMA FLOPs counted / FLOPs by the metric convention: {flops / w.flops:.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_INSTS_LDS"):
+        derived.append(f"LDS bank conflict cycles per LDS instruction: {mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_INSTS_LDS']:.4f}")
+    trace = os.path.join(PROFILES, f"kernel_trace_{workload_name}.txt")
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and os.path.exists(trace):
+        with open(trace) as f:
+            row = next((ln for ln in f if ln.startswith("fa::fa_fwd_kernel")), None)
+        if row:
+            avg_us = float(row.split()[-4])
+            busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * avg_us * 1e3 * SPEC_CLOCK_GHZ)
+            derived.append(f"MFMA busy fraction over {SIMDS} SIMDs at {SPEC_CLOCK_GHZ} GHz for the traced mean "
+                           f"duration {avg_us:.2f} us: {busy:.3f}")
+    lines += ["", "derived:"] + [f"- {d}" for d in derived]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"counters_{workload_name}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, workload_name, command, prefix="kernel_trace"):
     """Write profiles/<prefix>_<workload>.txt from a rocprofv3 --kernel-trace --stats run."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
@@ -504,12 +544,17 @@ def main():
                     help="time only fa_bwd on --workload and print its line (for profiling runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/counters_<NAME>.txt from rocprofv3 --pmc passes over --workload")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--summary-prefix", default="kernel_trace", help="file name prefix of --summarize-trace")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.command)
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.workload, args.command, args.summary_prefix)
