@@ -36,7 +36,7 @@ read once) against the 8 TB/s peak.  ``cold``: the GPT-2- and BERT-shaped
 forward workloads (whose inputs fit in the 256 MiB MALL) timed with a 512 MiB
 device write before every launch, p10/p50/p90 of single launches.  ``gpu``:
 the device name, architecture and compute units, and the current clock
-levels from the driver's sysfs files right after the timed region.
+levels from the driver's sysfs files right after the headline's timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
     python bench.py --backward-only --workload NAME   time only fa_bwd on NAME (for profiling runs)
@@ -234,15 +234,28 @@ def backward_flops(w):
     return 2.5 * w.flops
 
 
+MIN_TIMED_MS = 200.0       # each timed region covers at least this long (auto step counts)
+AUTO_STEPS = (20, 5000)    # bounds of an automatic step count
+
+
 def time_launch(launch, steps, warmup, settle_s=0.25, graph=False):
+    """steps=None: as many steps as fill MIN_TIMED_MS, from the mean of the
+    last settling round (within AUTO_STEPS)."""
     import torch
     # untimed: let the clocks settle on this very step, then the W warmup steps
     torch.cuda.synchronize()
     t_end = time.perf_counter() + settle_s
-    while time.perf_counter() < t_end:
+    round_ms = None
+    while True:
+        r0 = time.perf_counter()
         for _ in range(8):
             launch()
         torch.cuda.synchronize()
+        round_ms = (time.perf_counter() - r0) * 1e3 / 8
+        if time.perf_counter() >= t_end:
+            break
+    if steps is None:
+        steps = int(min(AUTO_STEPS[1], max(AUTO_STEPS[0], math.ceil(MIN_TIMED_MS / max(round_ms, 1e-3)))))
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
@@ -264,7 +277,8 @@ def time_launch(launch, steps, warmup, settle_s=0.25, graph=False):
         t1 = time.perf_counter()
         per = a.elapsed_time(b) / steps
         return {"wall_ms_per_step": (t1 - t0) * 1e3 / steps, "kernel_ms_mean": per, "kernel_ms_median": per,
-                "kernel_ms_p10": None, "kernel_ms_p90": None, "timing": f"one HIP graph replay of {steps} launches"}
+                "kernel_ms_p10": None, "kernel_ms_p90": None, "steps": steps,
+                "timing": f"one HIP graph replay of {steps} launches"}
     # the timed region: exactly `steps` back-to-back launches, one event pair on
     # the launch stream around them and the host clock outside
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -293,6 +307,7 @@ def time_launch(launch, steps, warmup, settle_s=0.25, graph=False):
         "kernel_ms_median": kms[len(kms) // 2],
         "kernel_ms_p10": kms[len(kms) // 10],
         "kernel_ms_p90": kms[(9 * len(kms)) // 10],
+        "steps": steps,
         "timing": "eager back-to-back launches, one event pair around the timed region; "
                   "p10/p50/p90 from a separate untimed pass with an event pair around each launch",
     }
@@ -527,7 +542,8 @@ def line_for(w, t, steps, warmup):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=10000,
+                    help="timed launches of the headline workload (the default covers about 0.2 s)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -583,6 +599,7 @@ def main():
                           "timing": bt["timing"]}), flush=True)
         return 0
     t = time_workload(w, args.steps, args.warmup, args.settle, graph=args.graph)
+    gpu = gpu_info()                    # clocks as the headline's timed region left them
     achieved, peak, ai = line_for(w, t, args.steps, args.warmup)
     value = w.flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
     traffic = traffic_for(w.name)
@@ -622,11 +639,12 @@ def main():
         for ow in WORKLOADS:
             if ow.name == w.name:
                 continue
-            ot = time_workload(ow, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle,
+            ot = time_workload(ow, None, max(3, args.warmup // 2), args.settle,
                                graph=args.graph)
             oa, opk, oai = line_for(ow, ot, 0, 0)
             others[ow.name] = {"tflops_kernel": round(oa, 1), "pct_of_dense_peak": round(100 * oa / opk, 2),
-                               "kernel_ms_median": round(ot["kernel_ms_median"], 4), "dtype": ow.dtype,
+                               "kernel_ms_median": round(ot["kernel_ms_median"], 4), "steps": ot["steps"],
+                               "dtype": ow.dtype,
                                "peak": opk}
         line["other_workloads"] = others
     if not args.no_cold and not args.only_headline:
@@ -635,9 +653,9 @@ def main():
         bwd = {}
         for name in BWD_WORKLOADS:
             bw = by_name(name)
-            bt = time_backward(bw, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle, graph=args.graph)
+            bt = time_backward(bw, None, max(3, args.warmup // 2), args.settle, graph=args.graph)
             tf = backward_flops(bw) / (bt["kernel_ms_mean"] * 1e-3) / 1e12
-            bwd[name] = {"ms_per_call": round(bt["kernel_ms_mean"], 4), "tflops": round(tf, 1),
+            bwd[name] = {"ms_per_call": round(bt["kernel_ms_mean"], 4), "tflops": round(tf, 1), "steps": bt["steps"],
                          "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2),
                          "flops": "2.5 x forward (five N x N x d products)",
                          "launches": "dQ (with the statistics), dK/dV (+ reduction for split grouped heads)"}
@@ -646,15 +664,15 @@ def main():
         var = {}
         for name in ("long_causal_bf16_b1h32n8192d128", "gpt2s_causal_bf16_b8h12n1024d64"):
             vw = by_name(name)
-            at = time_alibi(vw, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle, graph=args.graph)
+            at = time_alibi(vw, None, max(3, args.warmup // 2), args.settle, graph=args.graph)
             tf = vw.flops / (at["kernel_ms_mean"] * 1e-3) / 1e12
             var["alibi:" + name] = {"ms_per_call": round(at["kernel_ms_mean"], 4), "tflops": round(tf, 1),
                                     "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}
         sw = by_name("long_causal_bf16_b1h32n8192d128").with_(causal=False)
         bm = local_global_mask(sw.N)
-        bt = time_blocksparse(sw, bm, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle,
+        bt = time_blocksparse(sw, bm, None, max(3, args.warmup // 2), args.settle,
                               graph=args.graph)
-        dt = time_workload(sw, max(10, args.steps // 4), max(3, args.warmup // 2), args.settle, graph=args.graph)
+        dt = time_workload(sw, None, max(3, args.warmup // 2), args.settle, graph=args.graph)
         tf = blocksparse_flops(sw, bm) / (bt["kernel_ms_mean"] * 1e-3) / 1e12
         var["blocksparse:local_global_b1h32n8192d128"] = {
             "ms_per_call": round(bt["kernel_ms_mean"], 4), "tflops_effective": round(tf, 1),
@@ -667,7 +685,7 @@ def main():
         from workloads import DECODE_WORKLOADS
         dec = {}
         for dw in DECODE_WORKLOADS:
-            dt = time_decode(dw, max(20, args.steps // 2), max(5, args.warmup), args.settle, graph=args.graph)
+            dt = time_decode(dw, None, max(5, args.warmup), args.settle, graph=args.graph)
             gbs = dw.compulsory_bytes / (dt["kernel_ms_mean"] * 1e-3) / 1e9
             dec[dw.name] = {"us_per_call": round(dt["kernel_ms_mean"] * 1e3, 1), "splits": dt["splits"],
                             "hbm_gbs": round(gbs, 0), "frac_of_hbm_peak": round(gbs / HBM_GBPS, 4),
@@ -676,7 +694,7 @@ def main():
         line["decode"] = dec
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
-    line["gpu"] = gpu_info()
+    line["gpu"] = gpu
     print(json.dumps(line), flush=True)
     return 0
 
