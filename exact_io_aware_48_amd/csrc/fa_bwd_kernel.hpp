@@ -384,13 +384,30 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   issue(0, slot(0));
   wait_vmcnt<0>();
   __syncthreads();
-  int cur = 0;
-  for (int it = 0; it < n_iter; ++it) {
-    if (it + 1 < n_iter) issue(it + 1, slot(cur ^ 1));
-    tile(it, slot(cur));
-    wait_vmcnt<0>();
-    __syncthreads();
-    cur ^= 1;
+  if constexpr (CAUSAL) {
+    // two-slot ring, unrolled by two so that the slot offsets are constants
+    // (not without the mask: those instances then need more registers)
+    auto step = [&](int it, int sl) __attribute__((always_inline)) {
+      if (it + 1 < n_iter) issue(it + 1, slot(sl ^ 1));
+      tile(it, slot(sl));
+      wait_vmcnt<0>();
+      __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < n_iter; it += 2) {
+      step(it, 0);
+      step(it + 1, 1);
+    }
+    if (it < n_iter) step(it, 0);
+  } else {
+    int cur = 0;
+    for (int it = 0; it < n_iter; ++it) {
+      if (it + 1 < n_iter) issue(it + 1, slot(cur ^ 1));
+      tile(it, slot(cur));
+      wait_vmcnt<0>();
+      __syncthreads();
+      cur ^= 1;
+    }
   }
 
   const float sc = p.scale;
