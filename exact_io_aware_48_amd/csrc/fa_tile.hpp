@@ -43,9 +43,19 @@ struct Tile {
     i32x4 l[MODE == MODE_F32 ? PV_STEPS : 1];
     i32x8 f8[MODE == MODE_FP8 ? PV_STEPS : 1];
   };
+  // d = 256, bf16: the operand reads of both products run PDEPTH MFMAs ahead
+  // (qk_pipe, pv_pipe).  The register file is full at two waves per SIMD,
+  // and left to itself the compiler keeps a single operand buffer, so that
+  // every MFMA waits for the LDS read issued just before it.  The read
+  // addresses are kept as few per-lane bases plus instruction immediates,
+  // which frees the registers the deeper pipeline needs.
+  static constexpr bool PIPE = MODE == MODE_BF16 && D == 256;
+  static constexpr int PDEPTH = 3;
   struct Lane {
     int n, hf;                  // query column, lane half
     int v_row, v_col;           // per-lane parts of the V^T transpose-read address
+    int ka[PIPE ? 8 : 1];       // PIPE: K-read offsets of d-steps c < 8 (step c + 8: +256 bytes)
+    int va[PIPE ? 4 : 1];       // PIPE: V^T-read offsets of d-blocks db < 4 (db + 4: +256 bytes)
   };
 
   static __device__ __forceinline__ Lane lane_info(int lane) {
@@ -60,6 +70,21 @@ struct Tile {
     } else {
       ln.v_row = 4 * ln.hf + ((lane >> 2) & 3);
       ln.v_col = 2 * (16 * (grp & 1) + 4 * (lane & 3));
+    }
+    if constexpr (PIPE) {
+      // K row n (+ 32 kb), chunk (2c + hf) ^ (n % 16): the swizzle leaves bit 4
+      // of the chunk index alone, so steps c and c + 8 are 256 bytes apart.
+      // V^T rows v_row (+ 8, + 16 s) share the swizzle 4 * (v_row % 4), which
+      // leaves bit 4 alone too, so d-blocks db and db + 4 are 256 bytes apart.
+      static_assert(G::CPR == 32, "PIPE addressing assumes 512-byte tile rows");
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        ln.ka[c] = ln.n * G::ROWB + (((2 * c + ln.hf) ^ swz_k<G::CPR>(ln.n)) << 4);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int col = 64 * db + ln.v_col;
+        ln.va[db] = ln.v_row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(ln.v_row)) << 4) | (col & 15));
+      }
     }
     return ln;
   }
@@ -161,8 +186,67 @@ struct Tile {
     else oacc[db] = mfma_bf16(a, __builtin_bit_cast(bf16x8, pf.h[s]), oacc[db]);
   }
 
+  // PIPE: the K operand of item i = (d-step c = i / KB, key block kb = i % KB)
+  static __device__ __forceinline__ bf16x8 k_operand_pipe(const char FA_LDS* kbase, int i, const Lane& ln) {
+    const int c = i / KB, kb = i % KB;
+    return __builtin_bit_cast(bf16x8, lds_read16(kbase + ln.ka[c & 7] + ((c >> 3) << 8) + kb * 32 * G::ROWB));
+  }
+  // PIPE: the V^T operand of item i = (key step s = i / NDB, d-block db = i % NDB)
+  static __device__ __forceinline__ bf16x8 v_operand_pipe(const char FA_LDS* vbase, int i, const Lane& ln) {
+    const int s = i / NDB, db = i % NDB;
+    const char FA_LDS* p = vbase + ln.va[db & 3] + ((db >> 2) << 8) + 16 * s * G::ROWB;
+    i16x4 lo = lds_tr16(p), hi = lds_tr16(p + 8 * G::ROWB);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // Scheduling groups (LLVM AMDGPU sched_group_barrier masks): R LDS reads
+  // per item, the first PDEPTH items' reads up front, then one MFMA and the
+  // reads of the item PDEPTH ahead, then the last PDEPTH MFMAs.
+  template <int NI, int R>
+  static __device__ __forceinline__ void pipe_schedule() {
+    constexpr int kMfma = 0x008, kDsRead = 0x100;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, R * PDEPTH, 0);
+#pragma unroll
+    for (int i = 0; i < NI - PDEPTH; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kMfma, PDEPTH, 0);
+  }
+  static __device__ __forceinline__ void qk_pipe(f32x16 (&st)[KB], const char FA_LDS* kbase, const QFrag& q, const Lane& ln) {
+    constexpr int NI = QK_STEPS * KB;
+    static_assert(NI > PDEPTH, "pipeline longer than the block");
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
+    bf16x8 a[PDEPTH];
+#pragma unroll
+    for (int i = 0; i < PDEPTH; ++i) a[i] = k_operand_pipe(kbase, i, ln);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      st[i % KB] = mfma_bf16(a[i % PDEPTH], q.a[i / KB], st[i % KB]);
+      if (i + PDEPTH < NI) a[i % PDEPTH] = k_operand_pipe(kbase, i + PDEPTH, ln);
+    }
+    pipe_schedule<NI, 1>();
+  }
+  static __device__ __forceinline__ void pv_pipe(f32x16 (&oacc)[NDB], const char FA_LDS* vbase, const PFrag& pf, const Lane& ln) {
+    constexpr int NI = PV_STEPS * NDB;
+    static_assert(NI > PDEPTH, "pipeline longer than the block");
+    bf16x8 a[PDEPTH];
+#pragma unroll
+    for (int i = 0; i < PDEPTH; ++i) a[i] = v_operand_pipe(vbase, i, ln);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      oacc[i % NDB] = mfma_bf16(a[i % PDEPTH], __builtin_bit_cast(bf16x8, pf.h[i / NDB]), oacc[i % NDB]);
+      if (i + PDEPTH < NI) a[i % PDEPTH] = v_operand_pipe(vbase, i + PDEPTH, ln);
+    }
+    pipe_schedule<NI, 2>();
+  }
+
   // st = K Q^T for the tile at kbase (rows: keys, columns: this wave's queries)
   static __device__ __forceinline__ void qk(f32x16 (&st)[KB], const char FA_LDS* kbase, const QFrag& q, const Lane& ln) {
+    if constexpr (PIPE) {
+      qk_pipe(st, kbase, q, ln);
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
 #pragma unroll
@@ -292,6 +376,10 @@ struct Tile {
 
   // oacc += V^T P^T for the tile at vbase
   static __device__ __forceinline__ void pv(f32x16 (&oacc)[NDB], const char FA_LDS* vbase, const PFrag& pf, const Lane& ln) {
+    if constexpr (PIPE) {
+      pv_pipe(oacc, vbase, pf, ln);
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < PV_STEPS; ++s) {
 #pragma unroll
