@@ -43,13 +43,13 @@ struct Tile {
     i32x4 l[MODE == MODE_F32 ? PV_STEPS : 1];
     i32x8 f8[MODE == MODE_FP8 ? PV_STEPS : 1];
   };
-  // d = 256, bf16: the operand reads of both products run PDEPTH MFMAs ahead
-  // (qk_pipe, pv_pipe).  The register file is full at two waves per SIMD,
-  // and left to itself the compiler keeps a single operand buffer, so that
-  // every MFMA waits for the LDS read issued just before it.  The read
-  // addresses are kept as few per-lane bases plus instruction immediates,
-  // which frees the registers the deeper pipeline needs.
-  static constexpr bool PIPE = MODE == MODE_BF16 && D == 256;
+  // bf16: the operand reads of both products run PDEPTH MFMAs ahead
+  // (qk_pipe, pv_pipe).  Left to itself the compiler keeps one or two
+  // operand buffers when registers are short (d = 256: one, so every MFMA
+  // waited for the LDS read issued just before it).  The read addresses are
+  // kept as a few per-lane bases plus instruction immediates, which frees the
+  // registers the deeper pipeline needs.  Depth 4 measured no faster than 3.
+  static constexpr bool PIPE = MODE == MODE_BF16;
   static constexpr int PDEPTH = 3;
   struct Lane {
     int n, hf;                  // query column, lane half
@@ -76,7 +76,9 @@ struct Tile {
       // of the chunk index alone, so steps c and c + 8 are 256 bytes apart.
       // V^T rows v_row (+ 8, + 16 s) share the swizzle 4 * (v_row % 4), which
       // leaves bit 4 alone too, so d-blocks db and db + 4 are 256 bytes apart.
-      static_assert(G::CPR == 32, "PIPE addressing assumes 512-byte tile rows");
+      // (Rows 32 kb + n and v_row + 16 s + 8 keep the same swizzle for every
+      // tile width used: 8, 16 or 32 chunks per row.)
+      static_assert(G::CPR == 8 || G::CPR == 16 || G::CPR == 32, "PIPE addressing: 128- to 512-byte tile rows");
 #pragma unroll
       for (int c = 0; c < 8; ++c)
         ln.ka[c] = ln.n * G::ROWB + (((2 * c + ln.hf) ^ swz_k<G::CPR>(ln.n)) << 4);
