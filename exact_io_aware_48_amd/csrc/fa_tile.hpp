@@ -49,13 +49,16 @@ struct Tile {
   // waited for the LDS read issued just before it).  The read addresses are
   // kept as a few per-lane bases plus instruction immediates, which frees the
   // registers the deeper pipeline needs.  Depth 4 measured no faster than 3.
-  static constexpr bool PIPE = MODE == MODE_BF16;
-  static constexpr int PDEPTH = 3;
+  // fp8 (operands of 8 registers, two or four reads each) pipelines two
+  // deep with the plain addressing, which fits its register budget.
+  static constexpr bool PIPE = MODE != MODE_F32;
+  static constexpr bool PIPE_ADDR = MODE == MODE_BF16;
+  static constexpr int PDEPTH = MODE == MODE_FP8 ? 2 : 3;
   struct Lane {
     int n, hf;                  // query column, lane half
     int v_row, v_col;           // per-lane parts of the V^T transpose-read address
-    int ka[PIPE ? 8 : 1];       // PIPE: K-read offsets of d-steps c < 8 (step c + 8: +256 bytes)
-    int va[PIPE ? 4 : 1];       // PIPE: V^T-read offsets of d-blocks db < 4 (db + 4: +256 bytes)
+    int ka[PIPE_ADDR ? 8 : 1];  // bf16: K-read offsets of d-steps c < 8 (step c + 8: +256 bytes)
+    int va[PIPE_ADDR ? 4 : 1];  // bf16: V^T-read offsets of d-blocks db < 4 (db + 4: +256 bytes)
   };
 
   static __device__ __forceinline__ Lane lane_info(int lane) {
@@ -71,7 +74,7 @@ struct Tile {
       ln.v_row = 4 * ln.hf + ((lane >> 2) & 3);
       ln.v_col = 2 * (16 * (grp & 1) + 4 * (lane & 3));
     }
-    if constexpr (PIPE) {
+    if constexpr (PIPE_ADDR) {
       // K row n (+ 32 kb), chunk (2c + hf) ^ (n % 16): the swizzle leaves bit 4
       // of the chunk index alone, so steps c and c + 8 are 256 bytes apart.
       // V^T rows v_row (+ 8, + 16 s) share the swizzle 4 * (v_row % 4), which
@@ -189,58 +192,65 @@ struct Tile {
   }
 
   // PIPE: the K operand of item i = (d-step c = i / KB, key block kb = i % KB)
-  static __device__ __forceinline__ bf16x8 k_operand_pipe(const char FA_LDS* kbase, int i, const Lane& ln) {
+  static __device__ __forceinline__ Op k_operand_pipe(const char FA_LDS* kbase, int i, const Lane& ln) {
     const int c = i / KB, kb = i % KB;
-    return __builtin_bit_cast(bf16x8, lds_read16(kbase + ln.ka[c & 7] + ((c >> 3) << 8) + kb * 32 * G::ROWB));
+    if constexpr (PIPE_ADDR)
+      return __builtin_bit_cast(bf16x8, lds_read16(kbase + ln.ka[c & 7] + ((c >> 3) << 8) + kb * 32 * G::ROWB));
+    else
+      return k_operand(kbase, c, kb, ln);
   }
   // PIPE: the V^T operand of item i = (key step s = i / NDB, d-block db = i % NDB)
-  static __device__ __forceinline__ bf16x8 v_operand_pipe(const char FA_LDS* vbase, int i, const Lane& ln) {
+  static __device__ __forceinline__ Op v_operand_pipe(const char FA_LDS* vbase, int i, const Lane& ln) {
     const int s = i / NDB, db = i % NDB;
-    const char FA_LDS* p = vbase + ln.va[db & 3] + ((db >> 2) << 8) + 16 * s * G::ROWB;
-    i16x4 lo = lds_tr16(p), hi = lds_tr16(p + 8 * G::ROWB);
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    if constexpr (PIPE_ADDR) {
+      const char FA_LDS* p = vbase + ln.va[db & 3] + ((db >> 2) << 8) + 16 * s * G::ROWB;
+      i16x4 lo = lds_tr16(p), hi = lds_tr16(p + 8 * G::ROWB);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return v_operand(vbase, s, db, ln);
+    }
   }
+  // LDS reads per operand
+  static constexpr int K_READS = MODE == MODE_FP8 ? 2 : 1, V_READS = MODE == MODE_FP8 ? 4 : 2;
   // Scheduling groups (LLVM AMDGPU sched_group_barrier masks): R LDS reads
   // per item, the first PDEPTH items' reads up front, then one MFMA and the
   // reads of the item PDEPTH ahead, then the last PDEPTH MFMAs.
   template <int NI, int R>
   static __device__ __forceinline__ void pipe_schedule() {
-    constexpr int kMfma = 0x008, kDsRead = 0x100;
-    __builtin_amdgcn_sched_group_barrier(kDsRead, R * PDEPTH, 0);
+    constexpr int kMfma = 0x008, kDsRead = 0x100, AHEAD = NI < PDEPTH ? NI : PDEPTH;
+    __builtin_amdgcn_sched_group_barrier(kDsRead, R * AHEAD, 0);
 #pragma unroll
-    for (int i = 0; i < NI - PDEPTH; ++i) {
+    for (int i = 0; i < NI - AHEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kMfma, PDEPTH, 0);
+    __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
   }
   static __device__ __forceinline__ void qk_pipe(f32x16 (&st)[KB], const char FA_LDS* kbase, const QFrag& q, const Lane& ln) {
     constexpr int NI = QK_STEPS * KB;
-    static_assert(NI > PDEPTH, "pipeline longer than the block");
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
-    bf16x8 a[PDEPTH];
+    Op a[PDEPTH];
 #pragma unroll
-    for (int i = 0; i < PDEPTH; ++i) a[i] = k_operand_pipe(kbase, i, ln);
+    for (int i = 0; i < PDEPTH && i < NI; ++i) a[i] = k_operand_pipe(kbase, i, ln);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      st[i % KB] = mfma_bf16(a[i % PDEPTH], q.a[i / KB], st[i % KB]);
+      qk_mma(st, i / KB, i % KB, a[i % PDEPTH], q);
       if (i + PDEPTH < NI) a[i % PDEPTH] = k_operand_pipe(kbase, i + PDEPTH, ln);
     }
-    pipe_schedule<NI, 1>();
+    pipe_schedule<NI, K_READS>();
   }
   static __device__ __forceinline__ void pv_pipe(f32x16 (&oacc)[NDB], const char FA_LDS* vbase, const PFrag& pf, const Lane& ln) {
     constexpr int NI = PV_STEPS * NDB;
-    static_assert(NI > PDEPTH, "pipeline longer than the block");
-    bf16x8 a[PDEPTH];
+    Op a[PDEPTH];
 #pragma unroll
-    for (int i = 0; i < PDEPTH; ++i) a[i] = v_operand_pipe(vbase, i, ln);
+    for (int i = 0; i < PDEPTH && i < NI; ++i) a[i] = v_operand_pipe(vbase, i, ln);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      oacc[i % NDB] = mfma_bf16(a[i % PDEPTH], __builtin_bit_cast(bf16x8, pf.h[i / NDB]), oacc[i % NDB]);
+      pv_mma(oacc, i / NDB, i % NDB, a[i % PDEPTH], pf);
       if (i + PDEPTH < NI) a[i % PDEPTH] = v_operand_pipe(vbase, i + PDEPTH, ln);
     }
-    pipe_schedule<NI, 2>();
+    pipe_schedule<NI, V_READS>();
   }
 
   // st = K Q^T for the tile at kbase (rows: keys, columns: this wave's queries)
