@@ -537,11 +537,13 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 s{}, dp{};
-#pragma unroll
-      for (int c = 0; c < NSTEP; ++c) {
-        s = mfma_bf16(row_operand<D>(ks, kb, c, ln), qf[c], s);
-        dp = mfma_bf16(row_operand<D>(vs, kb, c, ln), of[c], dp);
-      }
+      // items 2c (S^T, K rows) and 2c + 1 (dP^T, V rows), operand reads three ahead
+      mfma_pipeline<2 * NSTEP, 3, 1, bf16x8>(
+          [&](int i) __attribute__((always_inline)) { return row_operand<D>((i & 1) ? vs : ks, kb, i >> 1, ln); },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            if (i & 1) dp = mfma_bf16(a, of[i >> 1], dp);
+            else s = mfma_bf16(a, qf[i >> 1], s);
+          });
       float pr[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2));
@@ -558,11 +560,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
           const int i0 = 8 * u + 2 * w;
           dsp[u][w] = (int)pack_bf16x2(pr[i0] * (dp[i0] - dd), pr[i0 + 1] * (dp[i0 + 1] - dd));
         }
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dq[db] = mfma_bf16(tr_operand<D>(ks, 2 * kb + u, db, ln), __builtin_bit_cast(bf16x8, dsp[u]), dq[db]);
+      // items u * NDB + db: key step u of the block into d-block db
+      mfma_pipeline<2 * NDB, 3, 2, bf16x8>(
+          [&](int i) __attribute__((always_inline)) { return tr_operand<D>(ks, 2 * kb + i / NDB, i % NDB, ln); },
+          [&](int i, const bf16x8& a) __attribute__((always_inline)) {
+            dq[i % NDB] = mfma_bf16(a, __builtin_bit_cast(bf16x8, dsp[i / NDB]), dq[i % NDB]);
+          });
     }
   };
 

@@ -158,6 +158,35 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// A block of NI independent-operand MFMA items whose A operands come from
+// LDS: read(i) returns item i's operand (R LDS reads), mma(i, a) issues its
+// MFMA.  The reads run DEPTH items ahead of the MFMAs, in a fixed order given
+// to the scheduler with sched_group_barrier (LLVM AMDGPU masks: 0x008 MFMA,
+// 0x100 LDS read): the first DEPTH items' reads, then one MFMA and the reads
+// of the item DEPTH ahead, then the last DEPTH MFMAs.  Without it the
+// compiler keeps as few operand buffers as registers force, and each MFMA
+// waits for the LDS read issued just before it.
+template <int NI, int DEPTH, int R, class Op, class Read, class Mma>
+__device__ __forceinline__ void mfma_pipeline(Read&& read, Mma&& mma) {
+  constexpr int AHEAD = NI < DEPTH ? NI : DEPTH;
+  Op a[AHEAD];
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) a[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    mma(i, a[i % AHEAD]);
+    if (i + AHEAD < NI) a[i % AHEAD] = read(i + AHEAD);
+  }
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, R * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NI - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
+}
+
 // round-to-nearest-even float -> bf16 bits (the hardware conversion)
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -212,45 +212,17 @@ struct Tile {
   }
   // LDS reads per operand
   static constexpr int K_READS = MODE == MODE_FP8 ? 2 : 1, V_READS = MODE == MODE_FP8 ? 4 : 2;
-  // Scheduling groups (LLVM AMDGPU sched_group_barrier masks): R LDS reads
-  // per item, the first PDEPTH items' reads up front, then one MFMA and the
-  // reads of the item PDEPTH ahead, then the last PDEPTH MFMAs.
-  template <int NI, int R>
-  static __device__ __forceinline__ void pipe_schedule() {
-    constexpr int kMfma = 0x008, kDsRead = 0x100, AHEAD = NI < PDEPTH ? NI : PDEPTH;
-    __builtin_amdgcn_sched_group_barrier(kDsRead, R * AHEAD, 0);
-#pragma unroll
-    for (int i = 0; i < NI - AHEAD; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
-  }
   static __device__ __forceinline__ void qk_pipe(f32x16 (&st)[KB], const char FA_LDS* kbase, const QFrag& q, const Lane& ln) {
-    constexpr int NI = QK_STEPS * KB;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) st[kb] = f32x16{};
-    Op a[PDEPTH];
-#pragma unroll
-    for (int i = 0; i < PDEPTH && i < NI; ++i) a[i] = k_operand_pipe(kbase, i, ln);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      qk_mma(st, i / KB, i % KB, a[i % PDEPTH], q);
-      if (i + PDEPTH < NI) a[i % PDEPTH] = k_operand_pipe(kbase, i + PDEPTH, ln);
-    }
-    pipe_schedule<NI, K_READS>();
+    mfma_pipeline<QK_STEPS * KB, PDEPTH, K_READS, Op>(
+        [&](int i) __attribute__((always_inline)) { return k_operand_pipe(kbase, i, ln); },
+        [&](int i, const Op& a) __attribute__((always_inline)) { qk_mma(st, i / KB, i % KB, a, q); });
   }
   static __device__ __forceinline__ void pv_pipe(f32x16 (&oacc)[NDB], const char FA_LDS* vbase, const PFrag& pf, const Lane& ln) {
-    constexpr int NI = PV_STEPS * NDB;
-    Op a[PDEPTH];
-#pragma unroll
-    for (int i = 0; i < PDEPTH && i < NI; ++i) a[i] = v_operand_pipe(vbase, i, ln);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      pv_mma(oacc, i / NDB, i % NDB, a[i % PDEPTH], pf);
-      if (i + PDEPTH < NI) a[i % PDEPTH] = v_operand_pipe(vbase, i + PDEPTH, ln);
-    }
-    pipe_schedule<NI, V_READS>();
+    mfma_pipeline<PV_STEPS * NDB, PDEPTH, V_READS, Op>(
+        [&](int i) __attribute__((always_inline)) { return v_operand_pipe(vbase, i, ln); },
+        [&](int i, const Op& a) __attribute__((always_inline)) { pv_mma(oacc, i / NDB, i % NDB, a, pf); });
   }
 
   // st = K Q^T for the tile at kbase (rows: keys, columns: this wave's queries)
