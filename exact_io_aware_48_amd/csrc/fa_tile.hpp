@@ -425,7 +425,14 @@ struct Tile {
 template <int D, int BC, int NW, int MODE, bool IS_V>
 struct Stager {
   using G = Geo<D, BC, NW, MODE>;
-  int ofs[G::UPT];
+  // Chunk i of a thread lies NW * 1024 bytes (ADV rows) after chunk 0.  When
+  // ADV is a multiple of the swizzle period (16 rows for every K and V
+  // swizzle here), chunk i has chunk 0's swizzle: its offset is chunk 0's
+  // plus a constant, and one register holds them all.
+  static constexpr int ADV = NW * 1024 / G::ROWB;
+  static constexpr bool AFFINE = NW * 1024 % G::ROWB == 0 && ADV % 16 == 0;
+  int ofs[AFFINE ? 1 : G::UPT];
+  int row0_, swz0_;   // AFFINE: chunk 0's row and swizzled byte column
 
   static __device__ __forceinline__ int swz(int row) {
     if constexpr (IS_V) return swz_v<G::CPR, MODE>(row);
@@ -433,10 +440,14 @@ struct Stager {
   }
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < G::UPT; ++i) {
+    for (int i = 0; i < (AFFINE ? 1 : G::UPT); ++i) {
       const int off = (i * NW + wave) * 1024 + lane * 16;
       const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
       ofs[i] = row * G::ROWB + ((pc ^ swz(row)) << 4);
+      if (i == 0) {
+        row0_ = row;
+        swz0_ = (pc ^ swz(row)) << 4;
+      }
     }
   }
   // tile j of the head at glob -> LDS at dst
@@ -446,14 +457,19 @@ struct Stager {
     const char* base = glob + (int64_t)row0 * G::ROWB;
     if (row0 + BC <= N) {
 #pragma unroll
-      for (int i = 0; i < G::UPT; ++i) dma16_s(base, ofs[i], dst + (i * NW + wave) * 1024);
+      for (int i = 0; i < G::UPT; ++i)
+        dma16_s(base, AFFINE ? ofs[0] + i * NW * 1024 : ofs[i], dst + (i * NW + wave) * 1024);
     } else {
       const int last = N - 1 - row0;
 #pragma unroll
       for (int i = 0; i < G::UPT; ++i) {
-        const int off = (i * NW + wave) * 1024 + lane * 16;
-        const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
-        dma16_s(base, min(row, last) * G::ROWB + ((pc ^ swz(row)) << 4), dst + (i * NW + wave) * 1024);
+        if constexpr (AFFINE) {
+          dma16_s(base, min(row0_ + i * ADV, last) * G::ROWB + swz0_, dst + (i * NW + wave) * 1024);
+        } else {
+          const int off = (i * NW + wave) * 1024 + lane * 16;
+          const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
+          dma16_s(base, min(row, last) * G::ROWB + ((pc ^ swz(row)) << 4), dst + (i * NW + wave) * 1024);
+        }
       }
     }
   }
