@@ -48,7 +48,7 @@ struct Tile {
   // operand buffers when registers are short (d = 256: one, so every MFMA
   // waited for the LDS read issued just before it).  The read addresses are
   // kept as a few per-lane bases plus instruction immediates, which frees the
-  // registers the deeper pipeline needs.  Depth 4 measured no faster than 3.
+  // registers the deeper pipeline needs.  Depths 2 and 4 measured the same as 3.
   // fp8 (operands of 8 registers, two or four reads each) pipelines two
   // deep with the plain addressing, which fits its register budget.
   static constexpr bool PIPE = MODE != MODE_F32;
