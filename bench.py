@@ -36,7 +36,7 @@ read once) against the 8 TB/s peak.  ``cold``: the GPT-2- and BERT-shaped
 forward workloads (whose inputs fit in the 256 MiB MALL) timed with a 512 MiB
 device write before every launch, p10/p50/p90 of single launches.  ``gpu``:
 the device name, architecture and compute units, and the current clock
-levels from the driver's sysfs files right after the headline's timed region.
+levels from the amdgpu kernel driver's sysfs files right after the headline's timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--only-headline]
     python bench.py --backward-only --workload NAME   time only fa_bwd on NAME (for profiling runs)
@@ -578,7 +578,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the attention forward shards over (batch, head) with no communication, so N GPUs would run "
               "N independent copies of this kernel on 1/N of the heads", file=sys.stderr)
         return 2
