@@ -344,17 +344,12 @@ def time_cold(w, iters=30, scratch_bytes=512 * 2**20):
             "iterations": iters, "eviction": f"{scratch_bytes >> 20} MiB device write before each launch"}
 
 
-def gpu_info():
-    """The GPU model (from the runtime) and the current clock levels from the
-    driver's sysfs files (pp_dpm_sclk / pp_dpm_mclk of each card it exposes,
-    read right after the timed region).  Plain file reads: nothing is spawned
-    from this GPU-initialised process."""
-    import torch
-    pr = torch.cuda.get_device_properties(0)
-    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
-            "memory_gib": round(pr.total_memory / 2**30, 1)}
+def read_clocks(kinds=("sclk", "mclk")):
+    """Current clock levels from the amdgpu kernel driver's sysfs files
+    (pp_dpm_sclk / pp_dpm_mclk of each card it exposes).  Plain file reads:
+    nothing is spawned from this GPU-initialised process."""
     clocks = {}
-    for kind in ("sclk", "mclk"):
+    for kind in kinds:
         for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}"))[:8]:
             try:
                 with open(path) as f:
@@ -363,7 +358,17 @@ def gpu_info():
                 continue
             cur = [ln.split(":", 1)[-1].replace("*", "").strip() for ln in levels if ln.rstrip().endswith("*")]
             clocks[f"{path.split('/')[4]}/{kind}"] = cur[0] if cur else None
-    info["clocks"] = clocks if clocks else "no readable /sys/class/drm/card*/device/pp_dpm_sclk"
+    return clocks if clocks else "no readable /sys/class/drm/card*/device/pp_dpm_sclk"
+
+
+def gpu_info():
+    """The GPU model (from the runtime) and the current clock levels, read
+    right after the headline's timed region."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1)}
+    info["clocks"] = read_clocks()
     return info
 
 
@@ -645,7 +650,8 @@ def main():
             others[ow.name] = {"tflops_kernel": round(oa, 1), "pct_of_dense_peak": round(100 * oa / opk, 2),
                                "kernel_ms_median": round(ot["kernel_ms_median"], 4), "steps": ot["steps"],
                                "dtype": ow.dtype,
-                               "peak": opk}
+                               "peak": opk,
+                               "sclk_after": read_clocks(("sclk",))}
         line["other_workloads"] = others
     if not args.no_cold and not args.only_headline:
         line["cold"] = {name: time_cold(by_name(name)) for name in COLD_WORKLOADS}
