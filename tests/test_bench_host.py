@@ -1,0 +1,89 @@
+"""Host logic of bench.py (CPU only): the one-GPU refusal, the staleness
+guard on recorded HBM traffic, and the rocprofv3 summary writers on small
+synthetic CSV files."""
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout.strip() == ""          # no JSON line for a refused run
+
+
+def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    name = "gpt2s_causal_bf16_b8h12n1024d64"
+    assert bench.traffic_for(name) is None                     # nothing recorded
+    rec = {"kernel_source_sha": bench.kernel_source_hash(), "hbm_bytes_per_launch": 123.0}
+    (tmp_path / f"traffic_{name}.json").write_text(json.dumps(rec))
+    assert bench.traffic_for(name) == 123.0
+    rec["kernel_source_sha"] = "0" * 16                         # recorded for other kernel sources
+    (tmp_path / f"traffic_{name}.json").write_text(json.dumps(rec))
+    assert bench.traffic_for(name) is None
+
+
+def test_kernel_source_hash_covers_the_forward_sources():
+    """The recorded traffic belongs to the forward kernel: every local file
+    the forward entry points are compiled from must be part of the hash."""
+    import re
+    dirs = [os.path.join(ROOT, "exact_io_aware_48_amd", "csrc"), os.path.join(ROOT, "include")]
+    seen, todo = set(), [os.path.join(dirs[0], "fa_api.hip")]
+    while todo:
+        path = todo.pop()
+        rel = os.path.relpath(path, ROOT)
+        if rel in seen:
+            continue
+        seen.add(rel)
+        for inc in re.findall(r'^#include "([^"]+)"', open(path).read(), re.M):
+            todo += [os.path.join(d, inc) for d in dirs if os.path.exists(os.path.join(d, inc))]
+    assert len(seen) >= 5
+    assert seen <= set(bench.KERNEL_SOURCES), sorted(seen - set(bench.KERNEL_SOURCES))
+
+
+def test_summarize_trace_writes_the_kernel_table(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    d = tmp_path / "trace" / "host" / "123"
+    d.mkdir(parents=True)
+    (d / "kt_kernel_stats.csv").write_text(
+        "Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs\n"
+        "\"void fa::fa_fwd_kernel<64, 64, 4, 0, true, false, 0, false>(fa::Params)\",10,230000,23000,100.0,20000,31000\n")
+    bench.summarize_trace(str(tmp_path / "trace"), "gpt2s_causal_bf16_b8h12n1024d64", "cmd")
+    text = (tmp_path / "profiles" / "kernel_trace_gpt2s_causal_bf16_b8h12n1024d64.txt").read_text()
+    row = next(ln for ln in text.splitlines() if ln.startswith("fa::fa_fwd_kernel"))
+    calls, avg, lo, hi, share = row.split()[-5:]
+    assert (int(calls), float(avg), float(lo), float(hi), float(share)) == (10, 23.0, 20.0, 31.0, 100.0)
+    assert f"kernel sources sha: {bench.kernel_source_hash()}" in text
+
+
+def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    name = "gpt2s_causal_bf16_b8h12n1024d64"
+    hdr = "Kernel_Name,Counter_Name,Counter_Value\n"
+    fetch, write = tmp_path / "f", tmp_path / "w"
+    fetch.mkdir()
+    write.mkdir()
+    # the copy of 256 MiB reads as 128 MiB in FETCH_SIZE (factor 2) and as 256 MiB in WRITE_SIZE
+    (fetch / "a_counter_collection.csv").write_text(
+        hdr + f"fa::fa_fwd_kernel<...>,FETCH_SIZE,1000\nfa::fa_fwd_kernel<...>,FETCH_SIZE,3000\n"
+              f"__amd_rocclr_copyBuffer,FETCH_SIZE,{128 * 1024}\n")
+    (write / "a_counter_collection.csv").write_text(
+        hdr + f"fa::fa_fwd_kernel<...>,WRITE_SIZE,500\n__amd_rocclr_copyBuffer,WRITE_SIZE,{256 * 1024}\n")
+    bench.summarize_pmc(str(fetch), str(write), name, "cmd")
+    rec = json.loads((tmp_path / "profiles" / f"traffic_{name}.json").read_text())
+    assert rec["copy_scale_fetch"] == pytest.approx(2.0)
+    assert rec["copy_scale_write"] == pytest.approx(1.0)
+    assert rec["hbm_bytes_per_launch"] == pytest.approx((2000 * 2.0 + 500 * 1.0) * 1024)
+    assert rec["kernel_source_sha"] == bench.kernel_source_hash()
