@@ -3,6 +3,10 @@
 max_abs   = max |O - O*|
 rel_l2    = ||O - O*||_F / ||O*||_F over the whole tensor
 lse_max   = max |L - L*|
+
+These are the tolerance metrics of the parity gate (maximum absolute error,
+relative L2 error over the whole tensor, largest logsumexp error).  Pinned by
+hand-computed cases and planted mistakes in tests/test_compare_pins.py.
 """
 
 import numpy as np
