@@ -51,6 +51,30 @@ def _check(t, name):
         raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
 
 
+def _check_out(t, name, shape, dtype, device):
+    """A caller-supplied output buffer: the kernels write shape-many dtype
+    elements through its pointer, so anything else is refused before a launch."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _outputs(o, lse, o_shape, o_dtype, lse_shape, device):
+    """Allocate o and lse when not given, else check them."""
+    o = torch.empty(o_shape, dtype=o_dtype, device=device) if o is None else _check_out(o, "o", o_shape, o_dtype, device)
+    lse = (torch.empty(lse_shape, dtype=torch.float32, device=device) if lse is None
+           else _check_out(lse, "lse", lse_shape, torch.float32, device))
+    return o, lse
+
+
 def _stream_ptr(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -76,10 +100,7 @@ def fa_fwd(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None):
         raise ValueError("q, k and v must have the same shape")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N), q.device)
     st = _lib.load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, H, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
                             _stream_ptr(stream))
@@ -100,10 +121,7 @@ def fa_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None, sc
         raise ValueError("q8, k8 and v8 must have the same shape")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    o, lse = _outputs(o, lse, (B, H, N, d), torch.bfloat16, (B, H, N), q8.device)
     st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                 B, H, N, d, float(scale), float(q_descale), float(k_descale),
                                 float(v_descale), int(bool(causal)), _stream_ptr(stream))
@@ -134,10 +152,7 @@ def fa_fwd_gqa(q, k, v, o=None, lse=None, scale=None, causal=False, stream=None)
     B, H, H_kv, N, d = _gqa_shapes(q, k, v, ("q", "k", "v"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N), q.device)
     st = _lib.load().fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                 B, H, H_kv, N, d, float(scale), int(bool(causal)), _DTYPE_CODE[q.dtype],
                                 _stream_ptr(stream))
@@ -156,10 +171,7 @@ def fa_fwd_gqa_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None
     B, H, H_kv, N, d = _gqa_shapes(q8, k8, v8, ("q8", "k8", "v8"))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if o is None:
-        o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    o, lse = _outputs(o, lse, (B, H, N, d), torch.bfloat16, (B, H, N), q8.device)
     st = _lib.load().fa_fwd_gqa_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                     B, H, H_kv, N, d, float(scale), float(q_descale), float(k_descale),
                                     float(v_descale), int(bool(causal)), _stream_ptr(stream))
@@ -187,8 +199,7 @@ def fa_fwd_alibi(q, k, v, slopes, o=None, lse=None, scale=None, causal=False, st
     slopes = slopes.contiguous()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N), q.device)
     st = _lib.load().fa_fwd_alibi(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                   slopes.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), _lib.FA_BF16,
                                   _stream_ptr(stream))
@@ -215,14 +226,24 @@ def fa_fwd_blocksparse(q, k, v, block_mask, o=None, lse=None, scale=None, causal
         raise ValueError("block_mask leading dimensions must be [B, H] or [H]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if o is None else o
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N), q.device)
     st = _lib.load().fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                         m.data_ptr(), sb, sh, B, H, N, d, float(scale), int(bool(causal)),
                                         _lib.FA_BF16, _stream_ptr(stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_blocksparse")
     return o, lse
+
+
+def _workspace(ws, need, device):
+    """A scratch buffer of at least need bytes on device (allocated when not given)."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.device != torch.device(device) or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds fewer than {need} bytes")
+    return ws
 
 
 def fa_bwd_workspace_size(B, H, H_kv, N, d):
@@ -254,17 +275,15 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if dq is None:
-        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    if dk is None:
-        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-    if dv is None:
-        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    if lse.device != q.device:
+        raise ValueError(f"lse must be on {q.device}")
+    grads = []
+    for g, nm, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        grads.append(torch.empty(ref.shape, dtype=torch.float32, device=q.device) if g is None
+                     else _check_out(g, nm, ref.shape, torch.float32, q.device))
+    dq, dk, dv = grads
     need = fa_bwd_workspace_size(B, H, H_kv, N, d)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace holds fewer than {need} bytes")
+    workspace = _workspace(workspace, need, q.device)
     st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                             workspace.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
                             float(scale), int(bool(causal)), _lib.FA_BF16, _stream_ptr(stream))
@@ -298,14 +317,8 @@ def fa_fwd_split(q, k, v, scale=None, causal=False, num_splits=0, o=None, lse=No
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     _, need = fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace holds fewer than {need} bytes")
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
+    o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N_q), q.device)
     st = _lib.load().fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                   workspace.data_ptr(), B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)),
                                   int(num_splits), _lib.FA_BF16, _stream_ptr(stream))
@@ -327,10 +340,7 @@ def fa_lse_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, o=None, lse=None,
     code = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_F32}.get(out_dtype)
     if code is None:
         raise ValueError("out_dtype must be bfloat16 or float32")
-    if o is None:
-        o = torch.empty((rows, d), dtype=out_dtype, device=o_parts.device)
-    if lse is None:
-        lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    o, lse = _outputs(o, lse, (rows, d), out_dtype, (rows,), o_parts.device)
     st = _lib.load().fa_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, rows, d, o.data_ptr(), lse.data_ptr(),
                                   code, _stream_ptr(stream))
     if st != _lib.FA_OK:
