@@ -1,6 +1,6 @@
 // C ABI of the FlashAttention forward library (declared in include/fa_fwd.h):
 // argument checks, choice of kernel instance, grid, launch.  No allocation,
-// no synchronisation, no state.
+// no synchronisation; the only state is the per-device residency cache (fa_host.hpp).
 #include <hip/hip_runtime.h>
 
 #include <cmath>

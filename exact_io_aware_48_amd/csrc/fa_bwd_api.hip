@@ -1,6 +1,7 @@
 // C ABI of the FlashAttention backward (declared in include/fa_bwd.h):
 // argument checks, kernel instances, grids and the three launches.  No
-// allocation, no synchronisation, no state; the caller provides the
+// allocation, no synchronisation; the only state is the per-device residency
+// cache (fa_host.hpp); the caller provides the
 // statistics workspace.
 #include <hip/hip_runtime.h>
 

@@ -1,6 +1,6 @@
 // C ABI of split-KV decode attention and the logsumexp merge (declared in
 // include/fa_split.h): argument checks, split plan, launches.  No
-// allocation, no synchronisation, no state.
+// allocation, no synchronisation, no state kept between calls.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -21,7 +21,8 @@
  * [B][H_kv][N][d]; lse: float32 [B][H][N] (natural log, as fa_fwd writes it).
  *
  * Memory and streams.  Every pointer is a device pointer owned by the caller;
- * the library allocates, frees and synchronises nothing and keeps no state.
+ * the library allocates, frees and synchronises nothing; like fa_fwd it keeps
+ * only a per-device cache of read-only launch facts (see fa_fwd.h).
  * ``workspace`` holds fa_bwd_workspace_size() bytes of per-row statistics
  * (and partial sums) that the call writes and then reads; its contents
  * before and after the call carry no meaning for the caller.  The work is

@@ -22,8 +22,13 @@
  * the key length.
  *
  * Memory and streams.  Every pointer is a device pointer owned by the caller;
- * the library never allocates, frees, synchronises or keeps state between
- * calls (all entry points are re-entrant).  ``stream`` is a hipStream_t
+ * the library never allocates, frees or synchronises.  The one thing it keeps
+ * between calls is a per-device, per-kernel cache of two read-only launch
+ * facts (how many workgroups of the kernel fit on the device at once, and the
+ * compute units per XCD), filled by the first call on a device.  It decides
+ * only the order in which workgroups are dealt to compute units, never a
+ * result, and it is written with atomic stores, so all entry points are
+ * re-entrant and thread-safe.  ``stream`` is a hipStream_t
  * (NULL = the default stream); the work is enqueued on it and the call
  * returns without waiting.  o and lse must not overlap q, k, v or each other.
  * Results are bitwise reproducible for equal inputs, shape and device.
