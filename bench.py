@@ -11,16 +11,25 @@ The K timed steps are K back-to-back launches of the entry point, bracketed by
 device synchronisation and one HIP event pair on the launch stream
 (``--graph``: captured once into a HIP graph and replayed).
 
-Prints one JSON line.  ``value`` is whole-job throughput in TFLOP/s by the
-convention 4*B*H*N^2*d (halved for the causal mask) over the K timed steps on
-the host clock.  ``roofline.achieved`` is the same FLOP count per launch over
-the mean launch duration from the HIP event pair around the timed region
-(divided by K; it includes whatever gap the GPU leaves between launches).
-``kernel_ms_p10_p50_p90`` comes from a separate untimed pass with an event pair
-around each launch, which itself adds dispatch latency.  ``traffic`` is the HBM bytes per launch measured with
-rocprofv3 PMC counters (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same
-counters give for a plain copy of known size), read from profiles/ and only
-when the kernel sources are unchanged since that measurement.
+Prints one JSON line.  The headline workload is the largest configuration of
+the metric's N = 1K-16K range (B=2, H=8, N=16384, d=256, bf16).  ``value`` is
+whole-job throughput in TFLOP/s by the convention 4*B*H*N^2*d (halved for the
+causal mask) over the K timed steps on the host clock.  ``roofline.achieved``
+is the same FLOP count per launch over the mean launch duration from the HIP
+event pair around the timed region (divided by K; it includes whatever gap the
+GPU leaves between launches).  ``kernel_ms_p10_p50_p90`` comes from a separate
+untimed pass with an event pair around each launch, which itself adds dispatch
+latency.  ``traffic`` is the HBM bytes per launch measured with rocprofv3 PMC
+counters (FETCH_SIZE + WRITE_SIZE, scaled by the factor the same counters give
+for a plain copy of known size), read from profiles/ and only when the kernel
+sources are unchanged since that measurement.
+
+``other_workloads`` times every other forward workload the same way and gives
+each its own ``roofline`` block.  The bound is the lower of the two ceilings:
+MFMA (the dense peak of the type the products use) or HBM at the compulsory
+traffic (Q, K, V read once, O and L written once).  An HBM-bound workload's
+block is in GB/s of compulsory bytes against 8 TB/s; its TFLOP/s and share of
+the dense peak are given beside it.
 
 The line also carries ``backward``: the mean time of one fa_bwd call (its
 launches back to back) on the long-context,
@@ -60,7 +69,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HEADLINE = "gpt2s_causal_bf16_b8h12n1024d64"
+HEADLINE = "wide_bf16_b2h8n16384d256"
 METRIC = "attention fwd TFLOP/s and % of MI355X dense MFMA peak at N=1K–16K, 1 GPU"
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 2516.6, "fp8": 5033.2}   # dense MFMA peaks of the type the products use
 HBM_GBPS = 8000.0
@@ -109,13 +118,14 @@ def device_inputs(w):
 
 
 def time_workload(w, steps, warmup, settle_s=0.25, graph=False):
-    """Time exactly `steps` launches of the forward on workload w.
+    """Time exactly `steps` launches of the forward on workload w (see time_launch).
 
-    graph=False (default): eager launches, one event pair around each launch;
-    the per-launch time is the mean over the pairs.
+    graph=False (default): `steps` eager launches back to back with one event
+    pair on the launch stream around all of them; the per-launch time is that
+    pair's time / steps.  A separate untimed pass brackets single launches with
+    their own event pairs for the spread (p10/p50/p90).
     graph=True: the `steps` launches are captured once into a HIP graph and the
-    timed region is one replay of it (the kernels run back to back, with no
-    host launch path in between); the per-launch time is the replay's event
+    timed region is one replay of it; the per-launch time is the replay's event
     time / steps, which includes the gap between dependent kernels.
     """
     import torch
@@ -383,25 +393,57 @@ def copy_calibration(nbytes=256 * 2**20, reps=3):
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
-def cpu_baseline(w, min_seconds=8.0):
-    """The float64 oracle, as it stands, over the whole workload, repeated until
-    ``min_seconds`` of wall time have passed (bounded: at most 100 passes)."""
+def cpu_share():
+    """The CPU threads this job may use: every core in the affinity mask, capped
+    by the CPU share the scheduler grants the job (OMP_NUM_THREADS when set;
+    one GPU's share on the GPU hosts)."""
+    cores = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    if share and share.isdigit() and int(share) > 0:
+        cores = min(cores, int(share))
+    return cores
+
+
+def blas_name():
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        return "unknown"
+
+
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
+    """The float64 oracle, as it stands, on a bounded sample of the workload:
+    whole heads (every query row against every key), one head after another in
+    the workload's order, until ``min_seconds`` of wall time have passed or the
+    workload is exhausted; TFLOP/s over the sample's own FLOPs."""
     from oracle import attention_naive
     from workloads import make_inputs
     x = make_inputs(w)
-    threads = min(16, len(os.sched_getaffinity(0)))
-    q, k, v = x.f64("q"), x.f64("k"), x.f64("v")
-    passes, t0 = 0, time.perf_counter()
-    while passes < 100:
-        attention_naive(q, k, v, w.softmax_scale, w.causal, threads=threads)
-        passes += 1
-        if time.perf_counter() - t0 >= min_seconds:
+    threads = cpu_share()
+    import numpy as np
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    head_flops = w.flops / len(heads)
+    # heads per oracle call: enough 1024-row chunks to keep every thread busy
+    per_call = max(1, math.ceil(2 * threads * 1024 / w.N))
+    done, t0 = 0, time.perf_counter()
+    for i in range(0, len(heads), per_call):
+        chunk = heads[i:i + per_call]
+        stack = lambda which, kv: np.stack([x.f64(which, b, h // w.group if kv else h) for b, h in chunk])[None]
+        attention_naive(stack("q", False), stack("k", True), stack("v", True), w.softmax_scale, w.causal,
+                        threads=threads)
+        done += len(chunk)
+        el = time.perf_counter() - t0
+        if el >= min_seconds or el + el * len(chunk) / done > max_seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(passes * w.flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} passes over the whole workload ({w.B}x{w.H} heads, N={w.N}, d={w.d}, "
-                      f"{'causal' if w.causal else 'full'}) in float64 numpy, {dt:.2f} s wall; "
-                      f"FLOPs by the same convention as value"}
+    return {"value": round(done * head_flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "blas": blas_name(),
+            "sample": f"{done} of the {len(heads)} heads of the workload (N={w.N}, d={w.d}, "
+                      f"{'causal' if w.causal else 'full'}, every row of each), float64 numpy oracle on "
+                      f"{threads} threads, {dt:.2f} s wall; FLOPs by the same convention as value"}
 
 
 # ------------------------------------------------------------------ PMC summary
@@ -537,17 +579,38 @@ def summarize_trace(trace_dir, workload_name, command, prefix="kernel_trace"):
 
 
 # ------------------------------------------------------------------ main
-def line_for(w, t, steps, warmup):
+def roofline_block(w, t):
+    """The roofline of one forward workload from its mean launch time.
+
+    Ceilings: the dense MFMA peak of the type the products use, and HBM at
+    the compulsory traffic (AI * 8 TB/s, AI = metric FLOPs / compulsory
+    bytes).  Whichever is lower bounds the kernel: an MFMA-bound block is in
+    TFLOP/s against the peak, an HBM-bound one in GB/s of compulsory bytes
+    against 8 TB/s."""
     peak = PEAK_TFLOPS[w.dtype]
-    achieved = w.flops / (t["kernel_ms_mean"] * 1e-3) / 1e12
+    sec = t["kernel_ms_mean"] * 1e-3
+    tflops = w.flops / sec / 1e12
     ai = w.flops / w.compulsory_bytes
-    return achieved, peak, ai
+    hbm_ceiling = ai * HBM_GBPS / 1e3
+    common = {"traffic": traffic_for(w.name), "kernel_ms_mean": round(t["kernel_ms_mean"], 5),
+              "tflops": round(tflops, 1), "pct_of_dense_peak": round(100 * tflops / peak, 2),
+              "arith_intensity_flop_per_compulsory_byte": round(ai, 1),
+              "ceilings_tflops": {"mfma": peak, "hbm": round(hbm_ceiling, 1)}}
+    if hbm_ceiling < peak:
+        gbs = w.compulsory_bytes / sec / 1e9
+        blk = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_GBPS, "unit": "GB/s",
+               "frac": round(gbs / HBM_GBPS, 4), "algorithmic_bytes_per_launch": w.compulsory_bytes}
+    else:
+        blk = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+               "frac": round(tflops / peak, 4), "algorithmic_flops_per_launch": w.flops}
+    blk.update(common)
+    return blk
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10000,
+    ap.add_argument("--steps", type=int, default=60,
                     help="timed launches of the headline workload (the default covers about 0.2 s)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
@@ -605,9 +668,12 @@ def main():
         return 0
     t = time_workload(w, args.steps, args.warmup, args.settle, graph=args.graph)
     gpu = gpu_info()                    # clocks as the headline's timed region left them
-    achieved, peak, ai = line_for(w, t, args.steps, args.warmup)
+    peak = PEAK_TFLOPS[w.dtype]
     value = w.flops / (t["wall_ms_per_step"] * 1e-3) / 1e12
-    traffic = traffic_for(w.name)
+    roof = roofline_block(w, t)
+    roof["kernel_ms_p10_p50_p90"] = None if t["kernel_ms_p10"] is None else \
+        [round(t["kernel_ms_p10"], 5), round(t["kernel_ms_median"], 5), round(t["kernel_ms_p90"], 5)]
+    roof["timing"] = t["timing"]
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -624,20 +690,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "scale": w.softmax_scale, "parallelism": "single GPU"},
         "pct_of_dense_peak": round(100 * value / peak, 2),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic,
-            "kernel_ms_mean": round(t["kernel_ms_mean"], 5),
-            "kernel_ms_p10_p50_p90": None if t["kernel_ms_p10"] is None else
-            [round(t["kernel_ms_p10"], 5), round(t["kernel_ms_median"], 5), round(t["kernel_ms_p90"], 5)],
-            "timing": t["timing"],
-            "arith_intensity_flop_per_compulsory_byte": round(ai, 1),
-            "hbm_ceiling_tflops": round(min(peak, ai * HBM_GBPS / 1e3), 1),
-        },
+        "roofline": roof,
+        "sclk_after": read_clocks(("sclk",)),
     }
     if not args.only_headline:
         others = {}
@@ -646,11 +700,11 @@ def main():
                 continue
             ot = time_workload(ow, None, max(3, args.warmup // 2), args.settle,
                                graph=args.graph)
-            oa, opk, oai = line_for(ow, ot, 0, 0)
-            others[ow.name] = {"tflops_kernel": round(oa, 1), "pct_of_dense_peak": round(100 * oa / opk, 2),
-                               "kernel_ms_median": round(ot["kernel_ms_median"], 4), "steps": ot["steps"],
-                               "dtype": ow.dtype,
-                               "peak": opk,
+            rb = roofline_block(ow, ot)
+            others[ow.name] = {"tflops_kernel": rb["tflops"], "pct_of_dense_peak": rb["pct_of_dense_peak"],
+                               "kernel_ms_mean": rb["kernel_ms_mean"],
+                               "kernel_ms_p50_single_launch": round(ot["kernel_ms_median"], 5),
+                               "steps": ot["steps"], "dtype": ow.dtype, "roofline": rb,
                                "sclk_after": read_clocks(("sclk",))}
         line["other_workloads"] = others
     if not args.no_cold and not args.only_headline:

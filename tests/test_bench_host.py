@@ -87,3 +87,41 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     assert rec["copy_scale_write"] == pytest.approx(1.0)
     assert rec["hbm_bytes_per_launch"] == pytest.approx((2000 * 2.0 + 500 * 1.0) * 1024)
     assert rec["kernel_source_sha"] == bench.kernel_source_hash()
+
+
+def test_roofline_block_bound_follows_the_lower_ceiling():
+    from workloads import by_name
+    # GPT-2-small shape: AI 254 FLOP/B, HBM ceiling 2032 < 2516.6 TFLOP/s -> HBM-bound, in GB/s
+    w = by_name("gpt2s_causal_bf16_b8h12n1024d64")
+    t = {"kernel_ms_mean": 0.025}
+    blk = bench.roofline_block(w, t)
+    assert blk["bound"] == "hbm" and blk["unit"] == "GB/s" and blk["peak"] == bench.HBM_GBPS
+    gbs = w.compulsory_bytes / 25e-6 / 1e9
+    assert abs(blk["achieved"] - gbs) < 0.1 and abs(blk["frac"] - gbs / 8000.0) < 1e-4
+    # the same fraction as TFLOP/s over the HBM ceiling
+    assert abs(blk["frac"] - blk["tflops"] / blk["ceilings_tflops"]["hbm"]) < 2e-3
+    # long causal d = 128: AI 2040 -> MFMA-bound against the bf16 peak
+    w = by_name("long_causal_bf16_b1h32n8192d128")
+    blk = bench.roofline_block(w, {"kernel_ms_mean": 0.5})
+    assert blk["bound"] == "mfma" and blk["unit"] == "TFLOP/s" and blk["peak"] == 2516.6
+    assert abs(blk["achieved"] - w.flops / 0.5e-3 / 1e12) < 0.01
+    # fp8 takes the fp8 peak
+    blk = bench.roofline_block(by_name("wide_fp8_b2h8n16384d256"), {"kernel_ms_mean": 2.0})
+    assert blk["bound"] == "mfma" and blk["peak"] == 5033.2
+
+
+def test_cpu_share_respects_the_granted_threads(monkeypatch):
+    cores = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    assert bench.cpu_share() == cores
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.cpu_share() == 1
+    monkeypatch.setenv("OMP_NUM_THREADS", str(cores + 100))
+    assert bench.cpu_share() == cores
+
+
+def test_headline_is_the_largest_metric_configuration():
+    from workloads import WORKLOADS, by_name
+    h = by_name(bench.HEADLINE)
+    assert h.dtype == "bf16"
+    assert all(h.flops >= w.flops for w in WORKLOADS if w.dtype == "bf16")
