@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libfa_fwd.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, f) for f in ("fa_api.hip", "fa_bwd_api.hip", "fa_split_api.hip")]
-HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp", "fa_bwd_kernel.hpp",
+HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp", "fa_pipe_kernel.hpp",
+                                           "fa_bwd_kernel.hpp",
                                            "fa_split_kernel.hpp", "fa_host.hpp")] + \
     [os.path.join(INCLUDE, h) for h in ("fa_fwd.h", "fa_bwd.h", "fa_split.h")]
 

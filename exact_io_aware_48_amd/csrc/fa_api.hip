@@ -8,9 +8,11 @@
 #include <algorithm>
 #include <climits>
 #include <atomic>
+#include <type_traits>
 
 #include "fa_fwd.h"
 #include "fa_fwd_kernel.hpp"
+#include "fa_pipe_kernel.hpp"
 #include "fa_host.hpp"
 
 namespace {
@@ -32,13 +34,15 @@ struct Tile {
 // within 256 VGPRs at two waves per SIMD.  PP: ping-pong wave groups (the
 // upper half of the waves runs P V one tile late), which pays off for fp8.
 // PRIO: raised wave priority outside the MFMA blocks (d = 256 bf16).
+// PIPE: the software-pipelined kernel (fa_pipe_kernel.hpp), whose waves weave
+// each tile's softmax into the neighbouring tiles' MFMAs (bf16, d = 128).
 template <int MODE, int D> struct Cfg;
-template <int BC_, int NW_, bool PP_, bool PRIO_ = false> struct Shape {
+template <int BC_, int NW_, bool PP_, bool PRIO_ = false, bool PIPE_ = false> struct Shape {
   static constexpr int BC = BC_, NW = NW_;
-  static constexpr bool PP = PP_, PRIO = PRIO_;
+  static constexpr bool PP = PP_, PRIO = PRIO_, PIPE = PIPE_;
 };
 template <> struct Cfg<fa::MODE_BF16, 64> : Shape<64, 4, false> {};
-template <> struct Cfg<fa::MODE_BF16, 128> : Shape<128, 8, false> {};
+template <> struct Cfg<fa::MODE_BF16, 128> : Shape<64, 8, false, false, true> {};
 template <> struct Cfg<fa::MODE_BF16, 256> : Shape<32, 8, false, true> {};
 template <> struct Cfg<fa::MODE_FP8, 64> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_FP8, 128> : Shape<64, 8, true> {};
@@ -46,6 +50,11 @@ template <> struct Cfg<fa::MODE_FP8, 256> : Shape<64, 8, true> {};
 template <> struct Cfg<fa::MODE_F32, 64> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_F32, 128> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_F32, 256> : Shape<32, 4, false> {};
+// The ALiBi and block-sparse variants are instances of fa_fwd_kernel; at
+// d = 128 they keep its measured shape (128-key tiles, the same 256-row
+// blocks as the pipelined kernel, so the grid is the same).
+template <int MODE, int D> struct VarCfg : Cfg<MODE, D> {};
+template <> struct VarCfg<fa::MODE_BF16, 128> : Shape<128, 8, false> {};
 
 template <int MODE, int D>
 Tile tile_for() {
@@ -69,9 +78,14 @@ Tile lookup_tile(int mode, int d) {
 
 template <int MODE, int D, bool CAUSAL, int VAR = fa::VAR_NONE>
 hipError_t launch(const Params& p, int grid, hipStream_t stream) {
-  using C = Cfg<MODE, D>;
+  using C = typename std::conditional<VAR == fa::VAR_NONE, Cfg<MODE, D>, VarCfg<MODE, D>>::type;
   constexpr int BC = C::BC, NW = C::NW;
-  void (*kern)(Params) = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR, VAR == fa::VAR_NONE && C::PRIO>;
+  static_assert(NW == Cfg<MODE, D>::NW, "variants and the plain kernel share the row-block size");
+  void (*kern)(Params);
+  if constexpr (VAR == fa::VAR_NONE && C::PIPE)
+    kern = &fa::fa_fwd_pipe_kernel<D, BC, NW, CAUSAL>;
+  else
+    kern = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR, VAR == fa::VAR_NONE && C::PRIO>;
   Params args = p;
   if constexpr (CAUSAL) {
     static std::atomic<int> cache[kMaxDevices];   // one per kernel
