@@ -5,7 +5,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_fwd.so")
 
-FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_HIP = range(7)
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_SCALE, FA_ERR_HIP, FA_ERR_SCRATCH = range(8)
 FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
 
 _lib = None
@@ -45,6 +45,10 @@ def load():
     lib.fa_fwd_split_plan.restype = i32
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.fa_fwd_split.restype = i32
+    lib.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp]
+    lib.fa_fwd_split_noalloc.restype = i32
+    lib.fa_split_scratch_bytes.argtypes = []
+    lib.fa_split_scratch_bytes.restype = i64
     lib.fa_lse_merge.argtypes = [vp, vp, i64, i64, i64, vp, vp, i32, vp]
     lib.fa_lse_merge.restype = i32
     lib.fa_version.argtypes = []

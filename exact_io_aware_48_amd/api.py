@@ -327,6 +327,38 @@ def fa_fwd_split(q, k, v, scale=None, causal=False, num_splits=0, o=None, lse=No
     return o, lse
 
 
+def fa_split_scratch_bytes():
+    """Size of the fixed device array fa_fwd_split_noalloc keeps its partials in."""
+    return int(_lib.load().fa_split_scratch_bytes())
+
+
+def fa_fwd_split_noalloc(q, k, v, o, lse, scale=None, causal=False, num_splits=0, stream=None):
+    """fa_fwd_split for callers that cannot allocate: the partials go to the
+    library's fixed per-GPU array instead of a workspace, and the outputs are
+    the caller's (o bfloat16 [B, H, N_q, d], lse float32 [B, H, N_q]).  Calls
+    that can overlap on one GPU race on that array.  Returns (o, lse)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16")
+    B, H, N_q, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must both be [B, H_kv, N_k, d] with q's B and d")
+    H_kv, N_k = k.shape[1], k.shape[2]
+    if o is None or lse is None:
+        raise ValueError("o and lse are the caller's buffers")
+    _check_out(o, "o", q.shape, q.dtype, q.device)
+    _check_out(lse, "lse", (B, H, N_q), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = _lib.load().fa_fwd_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                          B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)), int(num_splits),
+                                          _lib.FA_BF16, _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_split_noalloc")
+    return o, lse
+
+
 def fa_lse_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, o=None, lse=None, stream=None):
     """Merge attention partials: o_parts float32 [S, rows, d], lse_parts float32 [S, rows].
     Returns (o [rows, d] of out_dtype (bfloat16 or float32), lse float32 [rows])."""

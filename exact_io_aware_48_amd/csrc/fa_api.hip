@@ -285,6 +285,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: every pointer must be 16-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and descales finite and > 0";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected the launch";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the call needs more partials than fa_fwd_split_noalloc's fixed scratch holds";
     default: return "unknown fa_status";
   }
 }

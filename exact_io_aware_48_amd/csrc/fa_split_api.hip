@@ -1,10 +1,13 @@
 // C ABI of split-KV decode attention and the logsumexp merge (declared in
 // include/fa_split.h): argument checks, split plan, launches.  No
-// allocation, no synchronisation, no state kept between calls.
+// allocation and no synchronisation.  fa_fwd_split_noalloc keeps its partials
+// in the file-scope device array `scratch` (one copy per GPU, held until the
+// process ends) and caches each device's address of it.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -13,10 +16,39 @@
 #include "fa_split_kernel.hpp"
 #include "fa_host.hpp"
 
+// Partials of fa_fwd_split_noalloc: a fixed device array instead of a
+// caller's workspace.  The split kernel writes every element of the partials a
+// call uses before the merge reads it, so no call needs it cleared.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 using fa::MergeParams;
 using fa::SplitParams;
+
+// Each device's address of `scratch` (the host-side name is only a stand-in
+// for it), looked up with that device current on its first call there.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 // Keys per tile per head dim: one wave per workgroup, 32 KiB of K/V ring, so
 // that five workgroups share a CU and keep enough of the K/V stream in flight.
@@ -130,20 +162,33 @@ fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int
   return FA_OK;
 }
 
-fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int64_t B,
-                       int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
-                       int num_splits, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_split with the partials either in the caller's workspace or, when
+// workspace is NULL, in `scratch` (fa_fwd_split_noalloc)
+fa_status run_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int64_t B,
+                    int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
+                    int num_splits, int dtype, void* stream) {
+  const bool use_scratch = workspace == nullptr;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   fa_status st = check_split_shape(B, H, H_kv, N_q, N_k, d, dtype);
   if (st != FA_OK) return st;
-  for (const void* ptr : {q, k, v, (const void*)o, (const void*)lse, (const void*)workspace})
+  for (const void* ptr : {q, k, v, (const void*)o, (const void*)lse})
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if (!use_scratch && !aligned16(workspace)) return FA_ERR_ALIGN;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   const double c2 = std::fabs((double)scale) * 1.4426950408889634;
   if (!std::isfinite((float)c2)) return FA_ERR_SCALE;
   Plan pl;
   st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, num_splits == 0 ? device_cus() : 256, &pl);
   if (st != FA_OK) return st;
+  if (use_scratch) {
+    if (pl.workspace_bytes > kScratchBytes) return FA_ERR_SCRATCH;
+    workspace = scratch_on_current_device();
+    if (!workspace) return FA_ERR_HIP;
+  }
 
   const int64_t rows_total = B * H * N_q;
   SplitParams p{};
@@ -170,6 +215,25 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
   e = launch_merge(p.o_part, p.lse_part, pl.splits, rows_total, d, o, lse, true, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int64_t B,
+                       int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
+                       int num_splits, int dtype, void* stream) {
+  if (!workspace) return FA_ERR_NULL;
+  return run_split(q, k, v, o, lse, workspace, B, H, H_kv, N_q, N_k, d, scale, causal, num_splits, dtype, stream);
+}
+
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                               int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
+                               int num_splits, int dtype, void* stream) {
+  return run_split(q, k, v, o, lse, nullptr, B, H, H_kv, N_q, N_k, d, scale, causal, num_splits, dtype, stream);
+}
+
+int64_t fa_split_scratch_bytes(void) { return kScratchBytes; }
 
 fa_status fa_lse_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t rows, int64_t d,
                        void* o, float* lse, int out_dtype, void* stream) {

@@ -55,7 +55,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 3, /* d not in {64, 128, 256}, or unknown dtype */
   FA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   FA_ERR_SCALE = 5,       /* scale not finite, or an fp8 descale not finite and > 0 */
-  FA_ERR_HIP = 6          /* the HIP runtime rejected the launch */
+  FA_ERR_HIP = 6,         /* the HIP runtime rejected the launch */
+  FA_ERR_SCRATCH = 7      /* fa_fwd_split_noalloc: the call needs more than the library's fixed scratch */
 } fa_status;
 
 typedef enum {

@@ -68,6 +68,30 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        float scale, int causal, int num_splits, int dtype, void* stream);
 
 /*
+ * fa_fwd_split_noalloc -- fa_fwd_split without a workspace argument, for
+ * callers that cannot allocate device memory (code being captured into a HIP
+ * graph, serving loops that must not call the allocator, harnesses that forbid
+ * it).  The partials go to a fixed array inside the library instead:
+ * fa_split_scratch_bytes() bytes (32 MiB) on each GPU the library runs on,
+ * held until the process ends.  A call whose partials (the workspace size
+ * fa_fwd_split_plan reports for the same arguments) exceed that returns
+ * FA_ERR_SCRATCH before launching anything.  The call itself allocates and
+ * frees nothing.
+ * Every call on one GPU uses that GPU's one array: calls that can overlap on
+ * the same GPU (on different streams, or from different threads without
+ * ordering) race on it and must be serialised by the caller.  Calls on
+ * different GPUs do not interfere.  Arguments, results, errors and the split
+ * count are those of fa_fwd_split; for the same split count the result is
+ * bitwise the same.
+ */
+fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                               int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale,
+                               int causal, int num_splits, int dtype, void* stream);
+
+/* fa_split_scratch_bytes -- the size of fa_fwd_split_noalloc's fixed array, in bytes. */
+int64_t fa_split_scratch_bytes(void);
+
+/*
  * fa_lse_merge -- the merge alone, for partials made elsewhere (for example
  * one per device of a sequence-parallel split):
  *   o_parts   : float32 [num_parts][rows][d], each part normalised over its keys

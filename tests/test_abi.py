@@ -32,8 +32,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_alibi",
-                                    "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
-                                    "fa_status_string", "fa_version"]
+                                    "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split",
+                                    "fa_fwd_split_noalloc", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
+                                    "fa_split_scratch_bytes", "fa_status_string", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(7):
+    for code in range(8):
         s = lib.fa_status_string(code).decode()
         assert s.startswith("FA_")
     assert lib.fa_status_string(99).decode() == "unknown fa_status"
@@ -231,3 +232,22 @@ def test_fa_fwd_blocksparse_validation(lib, kw, expected):
     args = [a[n] for n in ("q", "k", "v", "o", "lse", "mask", "sb", "sh", "B", "H", "N", "d", "scale", "causal",
                            "dtype")]
     assert lib.fa_fwd_blocksparse(*args, None) == expected
+
+
+def test_split_noalloc_rejects_oversized_requests_before_any_launch(lib):
+    cap = lib.fa_split_scratch_bytes()
+    assert cap == 32 << 20
+    # 64 splits of B*H*N_q = 8192 rows at d = 128 need 64 * 8192 * 129 * 4 bytes > 32 MiB
+    need = ctypes.c_int64()
+    st = lib.fa_fwd_split_plan(8, 1024, 1024, 1, 65536, 128, 64, 1, None, ctypes.byref(need))
+    assert st == 0 and need.value > cap
+    st = lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 1024, 1024, 1, 65536, 128, 0.1, 1, 64, 1, None)
+    assert st == 7
+    assert lib.fa_status_string(7).decode().startswith("FA_ERR_SCRATCH")
+    # argument errors keep fa_fwd_split's codes
+    assert lib.fa_fwd_split_noalloc(0, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 1
+    assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 2, 1, 128, 0.1, 1, 0, 1, None) == 2
+    assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 256, 0.1, 1, 0, 1, None) == 3
+    assert lib.fa_fwd_split_noalloc(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 4
+    # fa_fwd_split still requires its workspace
+    assert lib.fa_fwd_split(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 1
