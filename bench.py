@@ -448,6 +448,11 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
 
 
 # ------------------------------------------------------------------ PMC summary
+def is_forward_kernel(name):
+    """The forward attention kernels (fa_fwd_kernel and the software-pipelined fa_fwd_pipe_kernel)."""
+    return "fa_fwd_kernel" in name or "fa_fwd_pipe_kernel" in name
+
+
 def _read_counter_csv(d):
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -466,11 +471,11 @@ def summarize_pmc(dir_fetch, dir_write, workload_name, command=""):
     out = {}
     for counter, d in (("FETCH_SIZE", dir_fetch), ("WRITE_SIZE", dir_write)):
         rows = [r for r in _read_counter_csv(d) if r.get("Counter_Name") == counter]
-        fa_vals = [float(r["Counter_Value"]) for r in rows if "fa_fwd_kernel" in r["Kernel_Name"]]
-        cp_vals = [float(r["Counter_Value"]) for r in rows if "fa_fwd_kernel" not in r["Kernel_Name"]
+        fa_vals = [float(r["Counter_Value"]) for r in rows if is_forward_kernel(r["Kernel_Name"])]
+        cp_vals = [float(r["Counter_Value"]) for r in rows if not is_forward_kernel(r["Kernel_Name"])
                    and "opy" in r["Kernel_Name"]]
         if not fa_vals:
-            raise SystemExit(f"no fa_fwd_kernel dispatch with {counter} in {d}")
+            raise SystemExit(f"no forward-kernel dispatch with {counter} in {d}")
         copy_kib = max(cp_vals) if cp_vals else None
         out[counter] = {"kib_per_dispatch_mean": sum(fa_vals) / len(fa_vals), "dispatches": len(fa_vals),
                         "copy_kib": copy_kib}
@@ -515,10 +520,10 @@ def summarize_counters(dirs, workload_name, command=""):
     vals = {}
     for d in dirs:
         for r in _read_counter_csv(d):
-            if "fa_fwd_kernel" in r["Kernel_Name"]:
+            if is_forward_kernel(r["Kernel_Name"]):
                 vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     if not vals:
-        raise SystemExit(f"no fa_fwd_kernel dispatch in {dirs}")
+        raise SystemExit(f"no forward-kernel dispatch in {dirs}")
     mean = {k: sum(v) / len(v) for k, v in sorted(vals.items())}
     lines = [f"# SQ counters of the forward kernel: {workload_name}", "",
              f"command (one pass per counter set): {command}", "",
@@ -540,7 +545,8 @@ def summarize_counters(dirs, workload_name, command=""):
     trace = os.path.join(PROFILES, f"kernel_trace_{workload_name}.txt")
     if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and os.path.exists(trace):
         with open(trace) as f:
-            row = next((ln for ln in f if ln.startswith("fa::fa_fwd_kernel")), None)
+            row = next((ln for ln in f if ln.startswith("fa::fa_fwd_kernel") or ln.startswith("fa::fa_fwd_pipe_kernel")),
+                       None)
         if row:
             avg_us = float(row.split()[-4])
             busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * avg_us * 1e3 * SPEC_CLOCK_GHZ)

@@ -57,6 +57,24 @@ def oracle_full(x: AttnInputs, scale=None):
     return o, l
 
 
+def oracle_threads():
+    """Threads for the float64 oracle: every core in the affinity mask, capped
+    by the CPU share the job is granted (OMP_NUM_THREADS when set)."""
+    import os
+    cores = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    return min(cores, int(share)) if share.isdigit() and int(share) > 0 else cores
+
+
+def oracle_all(x, scale=None):
+    """The float64 oracle over every element of the workload, threaded over
+    (batch, head, row chunk)."""
+    from oracle import attention_gqa
+    w = x.workload
+    scale = w.softmax_scale if scale is None else scale
+    return attention_gqa(x.f64("q"), x.f64("k"), x.f64("v"), scale, w.causal, threads=oracle_threads())
+
+
 def sample_rows(N, bc=64, br=128, count=48, seed=0):
     """Query rows worth checking: both ends, tile and row-block edges, and random ones."""
     rng = np.random.default_rng(seed)

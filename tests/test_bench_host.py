@@ -125,3 +125,10 @@ def test_headline_is_the_largest_metric_configuration():
     h = by_name(bench.HEADLINE)
     assert h.dtype == "bf16"
     assert all(h.flops >= w.flops for w in WORKLOADS if w.dtype == "bf16")
+
+
+def test_summaries_recognise_both_forward_kernels():
+    assert bench.is_forward_kernel("void fa::fa_fwd_kernel<64, 64, 4, 0, true, false, 0, false>(fa::Params)")
+    assert bench.is_forward_kernel("void fa::fa_fwd_pipe_kernel<128, 64, 8, true>(fa::Params)")
+    assert not bench.is_forward_kernel("void fa::fa_bwd_dq_kernel<128, 8, true>(fa::BwdParams)")
+    assert not bench.is_forward_kernel("__amd_rocclr_copyBuffer")
