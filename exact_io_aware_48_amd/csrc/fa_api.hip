@@ -172,7 +172,7 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   // exponentials at exactly 0.  For |scale| this small every product
   // |score| * c2 is far below one fp32 ulp of 1, so flooring it changes nothing.
   p.c2 = std::max((float)c2, 1e-30f);
-  p.out_mul = mode == fa::MODE_FP8 ? dv / 256.f : 1.f;
+  p.out_mul = mode == fa::MODE_FP8 ? dv : 1.f;
   p.qsign = 0;
   if (scale < 0.f) p.qsign = mode == fa::MODE_BF16 ? 0x80008000u : mode == fa::MODE_FP8 ? 0x80808080u : 1u;
 

@@ -25,7 +25,7 @@ struct Params {
   int cus_per_xcd; // compute units per XCD (0: unknown)
   int zigzag;      // causal grid fully resident: deal row blocks to CUs zig-zag (see map_block)
   float c2;        // |scale| * descale_q * descale_k * log2(e)
-  float out_mul;   // factor applied to O before dividing by l (fp8: descale_v / 256)
+  float out_mul;   // factor applied to O before dividing by l (fp8: descale_v)
   uint32_t qsign;  // XOR mask on Q's sign bits (negative scale)
   // variants (VAR_ALIBI, VAR_BLOCKSPARSE); unused otherwise
   int H;                   // query heads per batch (head index = bh % H)

@@ -28,6 +28,11 @@ struct Tile {
   static constexpr int PV_STEPS = MODE == MODE_FP8 ? BC / 64 : BC / 16; // MFMA k-steps over keys
   // lazy-rescale threshold (log2 units); fp8 keeps P <= 1 so that 256 * P fits e4m3
   static constexpr float TAU = MODE == MODE_FP8 ? 0.f : 8.f;
+  // fp8: P is stored as e4m3 of 256 * P (2^8 keeps small probabilities out of
+  // e4m3's subnormal range); the factor is taken into the exponent base, so
+  // the exponentials produce 256 * P directly and l sums 256 * P as well.  O
+  // is unchanged (the factor cancels in O / l) and L subtracts it back.
+  static constexpr float EXP_SHIFT = MODE == MODE_FP8 ? 8.f : 0.f;
 
   // the wave's 32 queries as the B operand of S^T = K Q^T
   struct QFrag {
@@ -313,7 +318,7 @@ struct Tile {
       sm.grow = m_tile > m_run + TAU;
       sm.alpha = sm.grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
       m_run = sm.grow ? m_tile : m_run;
-      sm.m_use = m_run == -INFINITY ? 0.f : m_run;
+      sm.m_use = m_run == -INFINITY ? 0.f : m_run - EXP_SHIFT;
     } else if constexpr (SL < NMAX + 1 + NEXP) {
       constexpr int g = SL - NMAX - 1;
       const int kb = g / 4, i0 = 4 * (g % 4);
@@ -331,8 +336,8 @@ struct Tile {
       if constexpr (MODE == MODE_FP8) {
         // step g/8, word g%8 <- scores 4g .. 4g+3 of the tile
         int word = 0;
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(x0 * 256.f, x1 * 256.f, word, false);
-        word = __builtin_amdgcn_cvt_pk_fp8_f32(x2 * 256.f, x3 * 256.f, word, true);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, word, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, word, true);
         pf.f8[g / 8][g % 8] = word;
       } else {
         // step g/2, words 2*(g%2) and 2*(g%2)+1 <- scores 4g .. 4g+3 of the tile
@@ -396,7 +401,8 @@ struct Tile {
     const bool seen = l_tot > 0.f;
     const float inv = seen ? p.out_mul / l_tot : 0.f;
     if (my_q >= p.N) return;
-    if (ln.hf == 0) p.lse[(int64_t)bh * p.N + my_q] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (ln.hf == 0)
+      p.lse[(int64_t)bh * p.N + my_q] = seen ? (m_run - EXP_SHIFT + __log2f(l_tot)) * kLn2 : -INFINITY;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
