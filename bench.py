@@ -79,7 +79,7 @@ BWD_WORKLOADS = ["long_causal_bf16_b1h32n8192d128", "gqa_causal_bf16_b1h32kv8n81
                  "gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64"]
 KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_tile.hpp",
                   "exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp", "exact_io_aware_48_amd/csrc/fa_pipe_kernel.hpp",
-                  "exact_io_aware_48_amd/csrc/fa_host.hpp",
+                  "exact_io_aware_48_amd/csrc/fa_host.hpp", "exact_io_aware_48_amd/csrc/fa_launch.hpp",
                   "exact_io_aware_48_amd/csrc/fa_api.hip", "include/fa_fwd.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 

@@ -37,6 +37,11 @@ def load():
     lib.fa_fwd_alibi.restype = i32
     lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, vp]
     lib.fa_fwd_blocksparse.restype = i32
+    lib.fa_fwd_alibi_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, f32, f32, f32, i32, vp]
+    lib.fa_fwd_alibi_fp8.restype = i32
+    lib.fa_fwd_blocksparse_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, f32, f32,
+                                           i32, vp]
+    lib.fa_fwd_blocksparse_fp8.restype = i32
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, pl]
     lib.fa_bwd_workspace_size.restype = i32
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i32, vp]

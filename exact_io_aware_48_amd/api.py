@@ -180,58 +180,117 @@ def fa_fwd_gqa_fp8(q8, k8, v8, q_descale, k_descale, v_descale, o=None, lse=None
     return o, lse
 
 
-def _bf16_square(q, k, v):
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+def _square(q, k, v, names=("q", "k", "v"), fp8=False):
+    """q, k, v of one shape and one dtype (the FP8 dtypes when fp8, else float32 or bfloat16)."""
+    for t, nm in zip((q, k, v), names):
         _check(t, nm)
-        if t.dtype != torch.bfloat16:
-            raise ValueError(f"{nm} must be bfloat16")
     if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k and v must have the same shape")
+        raise ValueError(f"{', '.join(names)} must have the same shape")
+    if fp8:
+        if any(t.dtype not in _FP8_DTYPES for t in (q, k, v)):
+            raise ValueError(f"{', '.join(names)} must be float8_e4m3fn or uint8 bytes")
+    elif q.dtype not in _DTYPE_CODE or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError(f"unsupported dtypes {q.dtype}/{k.dtype}/{v.dtype}")
     return q.shape
+
+
+def _slopes(slopes, H):
+    if (not isinstance(slopes, torch.Tensor) or slopes.dtype != torch.float32 or tuple(slopes.shape) != (H,)
+            or slopes.device.type != "cuda"):
+        raise ValueError("slopes must be a float32 device tensor [H]")
+    return slopes.contiguous()
+
+
+def _block_mask(block_mask, B, H, N):
+    """(mask, stride_b, stride_h) for a [B, H, nb, nb], [H, nb, nb] or [nb, nb] block mask."""
+    nb = (N + 127) // 128
+    m = block_mask
+    if not isinstance(m, torch.Tensor):
+        raise ValueError("block_mask must be a tensor")
+    if m.dtype == torch.bool:
+        m = m.to(torch.uint8)
+    if m.dtype != torch.uint8 or m.device.type != "cuda" or m.dim() < 2 or m.dim() > 4 or \
+            tuple(m.shape[-2:]) != (nb, nb):
+        raise ValueError(f"block_mask must be a uint8 device tensor [..., {nb}, {nb}]")
+    if m.dim() >= 3 and m.shape[-3] != H or m.dim() == 4 and m.shape[0] != B:
+        raise ValueError("block_mask leading dimensions must be [B, H] or [H]")
+    m = m.contiguous()
+    sb = nb * nb * m.shape[-3] if m.dim() == 4 else 0
+    sh = nb * nb if m.dim() >= 3 else 0
+    return m, sb, sh
 
 
 def fa_fwd_alibi(q, k, v, slopes, o=None, lse=None, scale=None, causal=False, stream=None):
     """fa_fwd with ALiBi biases -slopes[h] * |i - j| on the scaled scores.
-    q, k, v: bfloat16 [B, H, N, d]; slopes: float32 device tensor [H].  Returns (o, lse)."""
-    B, H, N, d = _bf16_square(q, k, v)
-    if slopes.dtype != torch.float32 or tuple(slopes.shape) != (H,) or slopes.device.type != "cuda":
-        raise ValueError("slopes must be a float32 device tensor [H]")
-    slopes = slopes.contiguous()
+    q, k, v: [B, H, N, d] of any fa_fwd dtype (FP8 with unit descales); slopes:
+    float32 device tensor [H].  Returns (o, lse)."""
+    if q.dtype in _FP8_DTYPES:
+        return fa_fwd_alibi_fp8(q, k, v, slopes, 1.0, 1.0, 1.0, o=o, lse=lse, scale=scale, causal=causal,
+                                stream=stream)
+    B, H, N, d = _square(q, k, v)
+    slopes = _slopes(slopes, H)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N), q.device)
     st = _lib.load().fa_fwd_alibi(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                  slopes.data_ptr(), B, H, N, d, float(scale), int(bool(causal)), _lib.FA_BF16,
-                                  _stream_ptr(stream))
+                                  slopes.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                  _DTYPE_CODE[q.dtype], _stream_ptr(stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_alibi")
+    return o, lse
+
+
+def fa_fwd_alibi_fp8(q8, k8, v8, slopes, q_descale, k_descale, v_descale, o=None, lse=None, scale=None,
+                     causal=False, stream=None):
+    """fa_fwd_alibi on FP8 (OCP e4m3fn) inputs with per-tensor descales; bfloat16 O, float32 lse."""
+    B, H, N, d = _square(q8, k8, v8, ("q8", "k8", "v8"), fp8=True)
+    slopes = _slopes(slopes, H)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse = _outputs(o, lse, (B, H, N, d), torch.bfloat16, (B, H, N), q8.device)
+    st = _lib.load().fa_fwd_alibi_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      slopes.data_ptr(), B, H, N, d, float(scale), float(q_descale),
+                                      float(k_descale), float(v_descale), int(bool(causal)), _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_alibi_fp8")
     return o, lse
 
 
 def fa_fwd_blocksparse(q, k, v, block_mask, o=None, lse=None, scale=None, causal=False, stream=None):
     """fa_fwd restricted to the allowed 128 x 128 blocks of block_mask, a uint8 (or
     bool) device tensor [B, H, nb, nb], [H, nb, nb] or [nb, nb] with nb = ceil(N / 128);
-    missing leading dimensions are shared.  Returns (o, lse)."""
-    B, H, N, d = _bf16_square(q, k, v)
-    nb = (N + 127) // 128
-    m = block_mask
-    if m.dtype == torch.bool:
-        m = m.to(torch.uint8)
-    if m.dtype != torch.uint8 or m.device.type != "cuda" or tuple(m.shape[-2:]) != (nb, nb) or m.dim() > 4:
-        raise ValueError(f"block_mask must be a uint8 device tensor [..., {nb}, {nb}]")
-    m = m.contiguous()
-    sb = nb * nb * m.shape[-3] if m.dim() == 4 else 0
-    sh = nb * nb if m.dim() >= 3 else 0
-    if m.dim() >= 3 and m.shape[-3] != H or m.dim() == 4 and m.shape[0] != B:
-        raise ValueError("block_mask leading dimensions must be [B, H] or [H]")
+    missing leading dimensions are shared.  Any fa_fwd dtype (FP8 with unit
+    descales).  Returns (o, lse)."""
+    if q.dtype in _FP8_DTYPES:
+        return fa_fwd_blocksparse_fp8(q, k, v, block_mask, 1.0, 1.0, 1.0, o=o, lse=lse, scale=scale,
+                                      causal=causal, stream=stream)
+    B, H, N, d = _square(q, k, v)
+    m, sb, sh = _block_mask(block_mask, B, H, N)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o, lse = _outputs(o, lse, q.shape, q.dtype, (B, H, N), q.device)
     st = _lib.load().fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                         m.data_ptr(), sb, sh, B, H, N, d, float(scale), int(bool(causal)),
-                                        _lib.FA_BF16, _stream_ptr(stream))
+                                        _DTYPE_CODE[q.dtype], _stream_ptr(stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_blocksparse")
+    return o, lse
+
+
+def fa_fwd_blocksparse_fp8(q8, k8, v8, block_mask, q_descale, k_descale, v_descale, o=None, lse=None, scale=None,
+                           causal=False, stream=None):
+    """fa_fwd_blocksparse on FP8 (OCP e4m3fn) inputs with per-tensor descales; bfloat16 O, float32 lse."""
+    B, H, N, d = _square(q8, k8, v8, ("q8", "k8", "v8"), fp8=True)
+    m, sb, sh = _block_mask(block_mask, B, H, N)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o, lse = _outputs(o, lse, (B, H, N, d), torch.bfloat16, (B, H, N), q8.device)
+    st = _lib.load().fa_fwd_blocksparse_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(),
+                                            lse.data_ptr(), m.data_ptr(), sb, sh, B, H, N, d, float(scale),
+                                            float(q_descale), float(k_descale), float(v_descale),
+                                            int(bool(causal)), _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_blocksparse_fp8")
     return o, lse
 
 

@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,11 +19,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_fwd.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, f) for f in ("fa_api.hip", "fa_bwd_api.hip", "fa_split_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fa_api.hip", "fa_var_api.hip", "fa_bwd_api.hip", "fa_split_api.hip")]
 HEADERS = [os.path.join(CSRC, h) for h in ("fa_common.hpp", "fa_tile.hpp", "fa_fwd_kernel.hpp", "fa_pipe_kernel.hpp",
-                                           "fa_bwd_kernel.hpp",
-                                           "fa_split_kernel.hpp", "fa_host.hpp")] + \
+                                           "fa_launch.hpp", "fa_bwd_kernel.hpp", "fa_split_kernel.hpp",
+                                           "fa_host.hpp")] + \
     [os.path.join(INCLUDE, h) for h in ("fa_fwd.h", "fa_bwd.h", "fa_split.h")]
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         # keep the compiler from forming packed-fp32 VALU ops
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc():
@@ -32,23 +36,36 @@ def hipcc():
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def compile_cmd(out=LIB, extra=()):
-    return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # keep the compiler from forming packed-fp32 VALU ops
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        f"-I{INCLUDE}", "-o", out, *SOURCES, *extra,
-    ]
+def compile_cmd(src, obj, extra=()):
+    """One translation unit to an object file."""
+    return [hipcc(), *FLAGS, f"-I{INCLUDE}", "-c", "-o", obj, src, *extra]
 
 
-def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = compile_cmd(tmp)
+def link_cmd(objs, out):
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
-    os.replace(tmp, LIB)
+
+
+def build(verbose=False, jobs=None):
+    """Compile every source (in parallel) and link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmpdir = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
+        jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            list(pool.map(_run, [compile_cmd(src, obj) for src, obj in zip(SOURCES, objs)]))
+        tmp = LIB + ".tmp"
+        _run(link_cmd(objs, tmp))
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     if verbose:
         print(f"built {LIB}")
     return LIB

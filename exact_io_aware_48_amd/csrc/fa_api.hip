@@ -11,105 +11,17 @@
 #include <type_traits>
 
 #include "fa_fwd.h"
-#include "fa_fwd_kernel.hpp"
-#include "fa_pipe_kernel.hpp"
-#include "fa_host.hpp"
+#include "fa_launch.hpp"
 
 namespace {
 
 using fa::Params;
-
-// A launch plan: tile shape and LDS footprint of the kernel instance used.
-struct Tile {
-  int bc;      // keys per K/V tile
-  int nw;      // waves per workgroup, 32 query rows each
-  int lds;     // LDS bytes per workgroup
-  int br() const { return 32 * nw; }
-};
-
-// Shape per (mode, d), chosen by measurement on MI355X.  Eight waves per
-// workgroup (256 query rows) halve the K/V traffic per FLOP for the large
-// heads; d = 64 keeps four waves so that the short causal rows spread over
-// more workgroups.  d = 256 with 16-bit tiles uses 32-key tiles to stay
-// within 256 VGPRs at two waves per SIMD.  PP: ping-pong wave groups (the
-// upper half of the waves runs P V one tile late), which pays off for fp8.
-// PRIO: raised wave priority outside the MFMA blocks (d = 256 bf16).
-// PIPE: the software-pipelined kernel (fa_pipe_kernel.hpp), whose waves weave
-// each tile's softmax into the neighbouring tiles' MFMAs (bf16, d = 128).
-template <int MODE, int D> struct Cfg;
-template <int BC_, int NW_, bool PP_, bool PRIO_ = false, bool PIPE_ = false> struct Shape {
-  static constexpr int BC = BC_, NW = NW_;
-  static constexpr bool PP = PP_, PRIO = PRIO_, PIPE = PIPE_;
-};
-template <> struct Cfg<fa::MODE_BF16, 64> : Shape<64, 4, false> {};
-template <> struct Cfg<fa::MODE_BF16, 128> : Shape<64, 8, false, false, true> {};
-template <> struct Cfg<fa::MODE_BF16, 256> : Shape<32, 8, false, true> {};
-template <> struct Cfg<fa::MODE_FP8, 64> : Shape<64, 4, false> {};
-template <> struct Cfg<fa::MODE_FP8, 128> : Shape<64, 8, true> {};
-template <> struct Cfg<fa::MODE_FP8, 256> : Shape<64, 8, true> {};
-template <> struct Cfg<fa::MODE_F32, 64> : Shape<64, 4, false> {};
-template <> struct Cfg<fa::MODE_F32, 128> : Shape<64, 4, false> {};
-template <> struct Cfg<fa::MODE_F32, 256> : Shape<32, 4, false> {};
-// The ALiBi and block-sparse variants are instances of fa_fwd_kernel; at
-// d = 128 they keep its measured shape (128-key tiles, the same 256-row
-// blocks as the pipelined kernel, so the grid is the same).
-template <int MODE, int D> struct VarCfg : Cfg<MODE, D> {};
-template <> struct VarCfg<fa::MODE_BF16, 128> : Shape<128, 8, false> {};
-
-template <int MODE, int D>
-Tile tile_for() {
-  using C = Cfg<MODE, D>;
-  return Tile{C::BC, C::NW, fa::Geo<D, C::BC, C::NW, MODE, C::PP>::LDSB};
-}
-
-Tile lookup_tile(int mode, int d) {
-  switch (mode) {
-    case fa::MODE_BF16:
-      return d == 64 ? tile_for<fa::MODE_BF16, 64>() : d == 128 ? tile_for<fa::MODE_BF16, 128>()
-                                                                 : tile_for<fa::MODE_BF16, 256>();
-    case fa::MODE_FP8:
-      return d == 64 ? tile_for<fa::MODE_FP8, 64>() : d == 128 ? tile_for<fa::MODE_FP8, 128>()
-                                                                : tile_for<fa::MODE_FP8, 256>();
-    default:
-      return d == 64 ? tile_for<fa::MODE_F32, 64>() : d == 128 ? tile_for<fa::MODE_F32, 128>()
-                                                                : tile_for<fa::MODE_F32, 256>();
-  }
-}
-
-template <int MODE, int D, bool CAUSAL, int VAR = fa::VAR_NONE>
-hipError_t launch(const Params& p, int grid, hipStream_t stream) {
-  using C = typename std::conditional<VAR == fa::VAR_NONE, Cfg<MODE, D>, VarCfg<MODE, D>>::type;
-  constexpr int BC = C::BC, NW = C::NW;
-  static_assert(NW == Cfg<MODE, D>::NW, "variants and the plain kernel share the row-block size");
-  void (*kern)(Params);
-  if constexpr (VAR == fa::VAR_NONE && C::PIPE)
-    kern = &fa::fa_fwd_pipe_kernel<D, BC, NW, CAUSAL>;
-  else
-    kern = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR, VAR == fa::VAR_NONE && C::PRIO>;
-  Params args = p;
-  if constexpr (CAUSAL) {
-    static std::atomic<int> cache[kMaxDevices];   // one per kernel
-    const Residency r = residency(reinterpret_cast<const void*>(kern), NW * 64, cache);
-    args.cus_per_xcd = r.cus_per_xcd;
-    args.zigzag = r.cus_per_xcd > 0 && grid <= r.resident ? 1 : 0;
-  }
-  void* kargs[] = {&args};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(NW * 64), kargs, 0, stream);
-}
 
 template <int MODE>
 hipError_t dispatch_d(const Params& p, int d, bool causal, int grid, hipStream_t s) {
   if (d == 64) return causal ? launch<MODE, 64, true>(p, grid, s) : launch<MODE, 64, false>(p, grid, s);
   if (d == 128) return causal ? launch<MODE, 128, true>(p, grid, s) : launch<MODE, 128, false>(p, grid, s);
   return causal ? launch<MODE, 256, true>(p, grid, s) : launch<MODE, 256, false>(p, grid, s);
-}
-
-// ALiBi and block-sparse variants: bf16 at d = 64 and 128
-template <int VAR>
-hipError_t dispatch_variant(const Params& p, int d, bool causal, int grid, hipStream_t s) {
-  if (d == 64)
-    return causal ? launch<fa::MODE_BF16, 64, true, VAR>(p, grid, s) : launch<fa::MODE_BF16, 64, false, VAR>(p, grid, s);
-  return causal ? launch<fa::MODE_BF16, 128, true, VAR>(p, grid, s) : launch<fa::MODE_BF16, 128, false, VAR>(p, grid, s);
 }
 
 // What a variant entry point adds to the plain forward.
@@ -147,7 +59,7 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   if (var.kind == fa::VAR_BLOCKSPARSE && !var.bmask) return FA_ERR_NULL;
   fa_status st = check_shape(B, H, N, d, dtype);
   if (st == FA_OK && (H_kv < 1 || H % H_kv != 0)) st = FA_ERR_SHAPE;
-  if (st == FA_OK && var.kind != fa::VAR_NONE && (dtype != FA_BF16 || (d != 64 && d != 128))) st = FA_ERR_UNSUPPORTED;
+  if (st == FA_OK && var.kind != fa::VAR_NONE && dtype == FA_F32 && d == 256) st = FA_ERR_UNSUPPORTED;
   if (st == FA_OK && var.kind == fa::VAR_BLOCKSPARSE && (var.sb < 0 || var.sh < 0)) st = FA_ERR_SHAPE;
   if (st != FA_OK) return st;
   if (var.kind == fa::VAR_ALIBI && (reinterpret_cast<uintptr_t>(var.slopes) & 3u)) return FA_ERR_ALIGN;
@@ -187,12 +99,8 @@ fa_status run(const void* q, const void* k, const void* v, void* o, float* lse, 
   const int grid = p.nrb * p.BH;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (var.kind == fa::VAR_ALIBI) {
-    e = dispatch_variant<fa::VAR_ALIBI>(p, (int)d, causal != 0, grid, s);
-    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
-  }
-  if (var.kind == fa::VAR_BLOCKSPARSE) {
-    e = dispatch_variant<fa::VAR_BLOCKSPARSE>(p, (int)d, causal != 0, grid, s);
+  if (var.kind != fa::VAR_NONE) {
+    e = fa_dispatch_variant(var.kind, mode, p, (int)d, causal != 0, grid, s);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
   }
   switch (mode) {
@@ -248,6 +156,29 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
   var.sb = mask_stride_b;
   var.sh = mask_stride_h;
   return run(q, k, v, o, lse, B, H, H, N, d, scale, 1.f, 1.f, 1.f, causal, dtype, stream, var);
+}
+
+fa_status fa_fwd_alibi_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                           const float* slopes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                           float q_descale, float k_descale, float v_descale, int causal, void* stream) {
+  Variant var;
+  var.kind = fa::VAR_ALIBI;
+  var.slopes = slopes;
+  return run(q8, k8, v8, o_bf16, lse, B, H, H, N, d, scale, q_descale, k_descale, v_descale, causal, FA_FP8_E4M3,
+             stream, var);
+}
+
+fa_status fa_fwd_blocksparse_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                                 const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, float scale, float q_descale, float k_descale,
+                                 float v_descale, int causal, void* stream) {
+  Variant var;
+  var.kind = fa::VAR_BLOCKSPARSE;
+  var.bmask = block_mask;
+  var.sb = mask_stride_b;
+  var.sh = mask_stride_h;
+  return run(q8, k8, v8, o_bf16, lse, B, H, H, N, d, scale, q_descale, k_descale, v_descale, causal, FA_FP8_E4M3,
+             stream, var);
 }
 
 fa_status fa_plan(int64_t B, int64_t H, int64_t N, int64_t d, int causal, int dtype, int* block_rows,

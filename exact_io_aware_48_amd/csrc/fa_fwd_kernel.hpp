@@ -71,7 +71,7 @@ namespace fa {
 template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false, int VAR = VAR_NONE, bool PRIO = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(Params p) {
-  static_assert(VAR == VAR_NONE || (MODE == MODE_BF16 && !PP), "variants: bf16, no ping-pong");
+  static_assert(VAR == VAR_NONE || !PP, "variants: no ping-pong");
   static_assert(VAR != VAR_BLOCKSPARSE || ((32 * NW) % kMaskBlock == 0 && kMaskBlock % BC == 0),
                 "row blocks and key tiles nest in the mask blocks");
   using G = Geo<D, BC, NW, MODE, PP>;
@@ -227,19 +227,31 @@ void fa_fwd_kernel(Params p) {
     };
     int j = next_needed(0);
     if (j < n_tiles) {
-      issue_tile(j, kslot(0), vslot(0));
-      wait_vmcnt<0>();
+      if constexpr (DMA) {
+        issue_tile(j, kslot(0), vslot(0));
+        wait_vmcnt<0>();
+      } else {
+        load_tile(j);
+        store_tile(kslot(0), vslot(0));
+      }
     }
     __syncthreads();
     int cur = 0;
     while (j < n_tiles) {
       const int jn = next_needed(j + 1);
-      if (jn < n_tiles) issue_tile(jn, kslot(cur ^ 1), vslot(cur ^ 1));
+      if (jn < n_tiles) {
+        if constexpr (DMA) issue_tile(jn, kslot(cur ^ 1), vslot(cur ^ 1));
+        else load_tile(jn);
+      }
       if (j < wave_tiles && allows(wblk, j)) {
         qk_softmax(j, kslot(cur));
         pv(vslot(cur));
       }
-      wait_vmcnt<0>();
+      if constexpr (DMA) {
+        wait_vmcnt<0>();
+      } else {
+        if (jn < n_tiles) store_tile(kslot(cur ^ 1), vslot(cur ^ 1));
+      }
       __syncthreads();
       cur ^= 1;
       j = jn;

@@ -50,9 +50,12 @@ void* scratch_on_current_device() {
   return g_scratch_ptr[dev];
 }
 
-// Keys per tile per head dim: one wave per workgroup, 32 KiB of K/V ring, so
-// that five workgroups share a CU and keep enough of the K/V stream in flight.
-int split_bc(int64_t d) { return d == 128 ? 32 : 64; }
+// Keys per tile per head dim: one wave per workgroup, 32 KiB of K/V ring at
+// d = 64 and 128, so that five workgroups share a CU and keep enough of the
+// K/V stream in flight.  d = 256 takes the smallest tile the 32 x 32 MFMA
+// allows (32 keys), a 64 KiB ring and two workgroups per CU.
+constexpr int split_bc_of(int d) { return d == 64 ? 64 : 32; }
+int split_bc(int64_t d) { return split_bc_of((int)d); }
 constexpr int kSplitNW = 1;
 constexpr int kRowsPerBlock = 32 * kSplitNW;
 
@@ -76,7 +79,7 @@ int device_cus() {
 
 fa_status check_split_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int dtype) {
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || N_q < 1 || N_k < N_q) return FA_ERR_SHAPE;
   if (B > INT_MAX / H) return FA_ERR_SHAPE;
   if (N_k > (int64_t)INT_MAX / (2 * d) || N_q > (int64_t)INT_MAX / (2 * d)) return FA_ERR_SHAPE;
@@ -123,7 +126,7 @@ constexpr int kSplitNS = 2;
 
 template <int D, bool CAUSAL>
 hipError_t launch_split(const SplitParams& p, int grid, hipStream_t stream) {
-  constexpr int BC = D == 128 ? 32 : 64;
+  constexpr int BC = split_bc_of(D);
   void (*kern)(SplitParams) = &fa::fa_split_kernel<D, BC, kSplitNW, kSplitNS, CAUSAL>;
   SplitParams args = p;
   void* kargs[] = {&args};
@@ -210,7 +213,8 @@ fa_status run_split(const void* q, const void* k, const void* v, void* o, float*
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d == 64) e = causal ? launch_split<64, true>(p, grid, s) : launch_split<64, false>(p, grid, s);
-  else e = causal ? launch_split<128, true>(p, grid, s) : launch_split<128, false>(p, grid, s);
+  else if (d == 128) e = causal ? launch_split<128, true>(p, grid, s) : launch_split<128, false>(p, grid, s);
+  else e = causal ? launch_split<256, true>(p, grid, s) : launch_split<256, false>(p, grid, s);
   if (e != hipSuccess) return FA_ERR_HIP;
   e = launch_merge(p.o_part, p.lse_part, pl.splits, rows_total, d, o, lse, true, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

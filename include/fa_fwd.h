@@ -132,12 +132,20 @@ fa_status fa_fwd_gqa_fp8(const void* q8, const void* k8, const void* v8, void* o
  * page says such masks need kernel variants; the bias form is the usual
  * ALiBi one.
  *   slopes : device float32 [H], finite, 4-byte aligned (FA_ERR_ALIGN), not NULL
- *   dtype  : FA_BF16 and d in {64, 128}, else FA_ERR_UNSUPPORTED
- * Otherwise as fa_fwd.
+ * Every dtype and head dim of fa_fwd except FA_F32 at d = 256
+ * (FA_ERR_UNSUPPORTED).  Otherwise as fa_fwd.
  */
 fa_status fa_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, const float* slopes,
                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
                        void* stream);
+
+/*
+ * fa_fwd_alibi on FP8 inputs with per-tensor descales, as fa_fwd_fp8: the
+ * score is scale * q_descale * k_descale * q8_i . k8_j - slopes[h] * |i - j|.
+ */
+fa_status fa_fwd_alibi_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                           const float* slopes, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                           float q_descale, float k_descale, float v_descale, int causal, void* stream);
 
 /*
  * fa_fwd_blocksparse -- fa_fwd restricted to the allowed blocks of a block
@@ -151,13 +159,19 @@ fa_status fa_fwd_alibi(const void* q, const void* k, const void* v, void* o, flo
  *   block_mask    : device bytes, nb x nb per (batch, head), not NULL
  *   mask_stride_b : bytes between batches' masks (0: one mask for all batches), >= 0
  *   mask_stride_h : bytes between heads' masks (0: one mask for all heads), >= 0
- *   dtype         : FA_BF16 and d in {64, 128}, else FA_ERR_UNSUPPORTED
- * Otherwise as fa_fwd.
+ * Every dtype and head dim of fa_fwd except FA_F32 at d = 256
+ * (FA_ERR_UNSUPPORTED).  Otherwise as fa_fwd.
  */
 fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                              const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h,
                              int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal, int dtype,
                              void* stream);
+
+/* fa_fwd_blocksparse on FP8 inputs with per-tensor descales, as fa_fwd_fp8. */
+fa_status fa_fwd_blocksparse_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
+                                 const uint8_t* block_mask, int64_t mask_stride_b, int64_t mask_stride_h,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                 float q_descale, float k_descale, float v_descale, int causal, void* stream);
 
 /*
  * fa_plan -- the launch fa_fwd / fa_fwd_fp8 (and their grouped-query

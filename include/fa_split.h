@@ -58,7 +58,7 @@ fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int
  *   workspace  : device memory of the size fa_fwd_split_plan reports for the
  *                same arguments; holds the partials (fp32 O_s, then L_s)
  *   N_q, N_k   : 1 <= N_q <= N_k, else FA_ERR_SHAPE
- *   d          : 64 or 128; dtype must be FA_BF16 (else FA_ERR_UNSUPPORTED)
+ *   d          : 64, 128 or 256; dtype must be FA_BF16 (else FA_ERR_UNSUPPORTED)
  *   scale      : any finite value; causal as described above
  *   num_splits : as for fa_fwd_split_plan
  * Every pointer must be 16-byte aligned.

@@ -32,7 +32,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_alibi",
-                                    "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split",
+                                    "fa_fwd_alibi_fp8", "fa_fwd_blocksparse", "fa_fwd_blocksparse_fp8", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split",
                                     "fa_fwd_split_noalloc", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
                                     "fa_split_scratch_bytes", "fa_status_string", "fa_version"]
 
@@ -178,18 +178,21 @@ def test_fa_fwd_split_plan(lib):
     assert st == 0 and sp == 1
     st, sp, _ = _plan(lib, 1, 8, 1, 1, 65536, 128, 0)
     assert st == 0 and 1 <= sp <= 2048 // 4
+    # d = 256 streams 32-key tiles too: 4096 keys asked in 4 splits -> 1024 keys each
+    st, sp, nb = _plan(lib, 1, 8, 2, 1, 4096, 256, 4)
+    assert st == 0 and sp == 4 and nb == 4 * 8 * 257 * 4
 
 
 @pytest.mark.parametrize("args,expected", [
     ((1, 8, 3, 1, 64, 64, 0), 2), ((1, 8, 8, 0, 64, 64, 0), 2), ((1, 8, 8, 65, 64, 64, 0), 2),
-    ((1, 8, 8, 1, 64, 64, -1), 2), ((1, 8, 8, 1, 64, 256, 0), 3), ((1, 8, 8, 1, 64, 64, 0, 0), 3),
+    ((1, 8, 8, 1, 64, 64, -1), 2), ((1, 8, 8, 1, 64, 512, 0), 3), ((1, 8, 8, 1, 64, 64, 0, 0), 3),
 ])
 def test_fa_fwd_split_plan_validation(lib, args, expected):
     assert _plan(lib, *args)[0] == expected
 
 
 @pytest.mark.parametrize("kw,expected", [
-    ({"q": 0}, 1), ({"ws": 0}, 1), ({"N_q": 5, "N_k": 4}, 2), ({"H_kv": 3}, 2), ({"d": 256}, 3), ({"dtype": 0}, 3),
+    ({"q": 0}, 1), ({"ws": 0}, 1), ({"N_q": 5, "N_k": 4}, 2), ({"H_kv": 3}, 2), ({"d": 512}, 3), ({"dtype": 0}, 3),
     ({"o": FAKE + 2}, 4), ({"ws": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
 ])
 def test_fa_fwd_split_validation(lib, kw, expected):
@@ -211,7 +214,8 @@ def test_fa_lse_merge_validation(lib, args, expected):
 
 
 @pytest.mark.parametrize("kw,expected", [
-    ({"slopes": 0}, 1), ({"q": 0}, 1), ({"dtype": 0}, 3), ({"dtype": 2}, 3), ({"d": 256}, 3), ({"N": 0}, 2),
+    ({"slopes": 0}, 1), ({"q": 0}, 1), ({"dtype": 3}, 3), ({"dtype": -1}, 3), ({"d": 96}, 3), ({"N": 0}, 2),
+    ({"dtype": 0, "d": 256}, 3),
     ({"slopes": FAKE + 2}, 4), ({"scale": float("inf")}, 5),
 ])
 def test_fa_fwd_alibi_validation(lib, kw, expected):
@@ -222,7 +226,8 @@ def test_fa_fwd_alibi_validation(lib, kw, expected):
 
 
 @pytest.mark.parametrize("kw,expected", [
-    ({"mask": 0}, 1), ({"o": 0}, 1), ({"sb": -1}, 2), ({"sh": -5}, 2), ({"dtype": 0}, 3), ({"d": 256}, 3),
+    ({"mask": 0}, 1), ({"o": 0}, 1), ({"sb": -1}, 2), ({"sh": -5}, 2), ({"dtype": 3}, 3), ({"d": 32}, 3),
+    ({"dtype": 0, "d": 256}, 3),
     ({"q": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
 ])
 def test_fa_fwd_blocksparse_validation(lib, kw, expected):
@@ -232,6 +237,32 @@ def test_fa_fwd_blocksparse_validation(lib, kw, expected):
     args = [a[n] for n in ("q", "k", "v", "o", "lse", "mask", "sb", "sh", "B", "H", "N", "d", "scale", "causal",
                            "dtype")]
     assert lib.fa_fwd_blocksparse(*args, None) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"slopes": 0}, 1), ({"v": 0}, 1), ({"d": 96}, 3), ({"H": 0}, 2), ({"slopes": FAKE + 1}, 4),
+    ({"dq": 0.0}, 5), ({"dk": -1.0}, 5), ({"dv": float("inf")}, 5), ({"scale": float("nan")}, 5),
+])
+def test_fa_fwd_alibi_fp8_validation(lib, kw, expected):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, slopes=FAKE, B=1, H=2, N=64, d=256, scale=0.1, dq=1.0,
+             dk=1.0, dv=1.0, causal=1)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "slopes", "B", "H", "N", "d", "scale", "dq", "dk", "dv",
+                           "causal")]
+    assert lib.fa_fwd_alibi_fp8(*args, None) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"mask": 0}, 1), ({"lse": 0}, 1), ({"sb": -1}, 2), ({"N": -4}, 2), ({"d": 512}, 3), ({"o": FAKE + 2}, 4),
+    ({"dq": -0.5}, 5), ({"dv": float("nan")}, 5),
+])
+def test_fa_fwd_blocksparse_fp8_validation(lib, kw, expected):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, mask=FAKE + 1, sb=0, sh=0, B=1, H=2, N=64, d=128, scale=0.1,
+             dq=1.0, dk=1.0, dv=1.0, causal=0)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "mask", "sb", "sh", "B", "H", "N", "d", "scale", "dq", "dk",
+                           "dv", "causal")]
+    assert lib.fa_fwd_blocksparse_fp8(*args, None) == expected
 
 
 def test_split_noalloc_rejects_oversized_requests_before_any_launch(lib):
@@ -247,7 +278,7 @@ def test_split_noalloc_rejects_oversized_requests_before_any_launch(lib):
     # argument errors keep fa_fwd_split's codes
     assert lib.fa_fwd_split_noalloc(0, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 1
     assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 2, 1, 128, 0.1, 1, 0, 1, None) == 2
-    assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 256, 0.1, 1, 0, 1, None) == 3
+    assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 96, 0.1, 1, 0, 1, None) == 3
     assert lib.fa_fwd_split_noalloc(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 4
     # fa_fwd_split still requires its workspace
     assert lib.fa_fwd_split(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 1

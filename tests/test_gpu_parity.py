@@ -71,6 +71,8 @@ def test_gqa_all_elements(name, B, H, H_kv, N, dtype, d, causal):
 EDGE = [(N, d, c, dt) for dt in ("bf16",) for d in (64, 128, 256) for N in (1, 7, 100, 257, 1000)
         for c in (False, True)]
 EDGE += [(N, d, c, "f32") for d in (64, 128, 256) for N in (1, 100, 257) for c in (False, True)]
+# fp32 at d = 256 runs its largest (spilling) instance: ragged causal diagonals at several sizes
+EDGE += [(N, 256, True, "f32") for N in (333, 1000, 1313)]
 EDGE += [(N, d, c, "fp8") for d in (64, 128, 256) for N in (1, 100, 257) for c in (False, True)]
 
 

@@ -52,6 +52,10 @@ CASES = [
     (1, 16, 2, 8, 500, 128, True, 3),         # 64 rows per K/V head: two row blocks
     (1, 2, 1, 1, 100, 64, True, 1000),        # more splits asked than tiles
     (3, 4, 4, 2, 3000, 64, False, 7),
+    (2, 8, 2, 1, 1000, 256, True, 0),         # d = 256: 32-key tiles, 64 KiB ring
+    (1, 16, 2, 8, 3001, 256, True, 3),
+    (1, 4, 4, 1, 20, 256, False, 1),
+    (2, 4, 1, 5, 2048, 256, False, 0),
 ]
 
 
