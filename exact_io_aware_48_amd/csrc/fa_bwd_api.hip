@@ -27,8 +27,8 @@ using fa::BwdParams;
 // per SIMD with K and V in VGPRs) serves small causal grids (launch_dkdv).
 // At d = 64 V stays in VGPRs.
 // dQ: NW waves of 32 queries, B_c-key K/V tiles.
-template <int NW_, int WPE_, bool VLDS_> struct KvShape {
-  static constexpr int NW = NW_, WPE = WPE_;
+template <int NW_, int WPE_, bool VLDS_, int KW_ = 32> struct KvShape {
+  static constexpr int NW = NW_, WPE = WPE_, KW = KW_;   // KW: keys per wave
   static constexpr bool VLDS = VLDS_;
 };
 template <int D> struct BwdCfg;
@@ -41,6 +41,15 @@ template <> struct BwdCfg<128> {
   using KV = KvShape<8, 2, true>;
   using KV_SMALL = KvShape<4, 1, false>;
   static constexpr int Q_BC = 64, Q_NW = 8, Q_WPE = 2;
+};
+// d = 256: a wave's dK and dV accumulators alone take 256 registers, so both
+// kernels run one wave per SIMD (the 512-register file), four waves per
+// workgroup; K and V stay in VGPRs (V in LDS would not fit beside the
+// 2 x 64 KiB Q/dO ring).
+template <> struct BwdCfg<256> {
+  using KV = KvShape<4, 1, false, 16>;
+  using KV_SMALL = KV;
+  static constexpr int Q_BC = 32, Q_NW = 4, Q_WPE = 1;
 };
 
 int64_t stat_tiles(int64_t N) { return (N + fa::kStatRows - 1) / fa::kStatRows; }
@@ -68,13 +77,13 @@ void set_balance(BwdParams& p, const void* kern, int threads, int grid, std::ato
 template <int D, bool CAUSAL, class S>
 hipError_t launch_dkdv_shape(const BwdParams& base, int64_t BHkv, int parts, hipStream_t stream) {
   BwdParams p = base;
-  constexpr int BK = 32 * S::NW;
+  constexpr int BK = S::KW * S::NW;
   p.BH = (int)(BHkv * parts);                // (K/V head, part) pairs
   p.parts = parts;
   p.nrb = (base.N + BK - 1) / BK;
   p.G = 1;
   p.xcd_heads = p.BH % 8 == 0 ? 1 : 0;
-  void (*kern)(BwdParams) = &fa::fa_bwd_dkdv_kernel<D, S::NW, S::WPE, CAUSAL, S::VLDS>;
+  void (*kern)(BwdParams) = &fa::fa_bwd_dkdv_kernel<D, S::NW, S::WPE, CAUSAL, S::VLDS, S::KW>;
   const int grid = p.nrb * p.BH;
   static std::atomic<int> cache[kMaxDevices];
   set_balance<CAUSAL>(p, reinterpret_cast<const void*>(kern), 64 * S::NW, grid, cache);
@@ -96,10 +105,10 @@ hipError_t launch_dkdv_shape(const BwdParams& base, int64_t BHkv, int parts, hip
 // grid takes the small shape instead.
 template <int D, bool CAUSAL, class BIG, class SMALL>
 hipError_t launch_dkdv(const BwdParams& base, int64_t BHkv, int G, hipStream_t stream) {
-  constexpr int BK = 32 * BIG::NW;
+  constexpr int BK = BIG::KW * BIG::NW;
   static std::atomic<int> cache[kMaxDevices];
   const Residency r = residency(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, BIG::NW, BIG::WPE, CAUSAL,
-                                                                                      BIG::VLDS>),
+                                                                                      BIG::VLDS, BIG::KW>),
                                 64 * BIG::NW, cache);
   const int64_t grid = (base.N + BK - 1) / BK * BHkv;
   const int64_t target = (CAUSAL ? 2 : 1) * (int64_t)r.resident;
@@ -142,7 +151,7 @@ hipError_t launch_bwd(const BwdParams& base, int64_t B, int64_t H, int64_t H_kv,
 
 fa_status check_bwd_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d, int dtype) {
   if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
   if (B > INT_MAX / H) return FA_ERR_SHAPE;                    // B*H fits an int
   if (N > (int64_t)INT_MAX / (2 * d)) return FA_ERR_SHAPE;     // one head's bytes fit an int
@@ -191,7 +200,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d == 64) e = causal ? launch_bwd<64, true>(p, B, H, H_kv, s) : launch_bwd<64, false>(p, B, H, H_kv, s);
-  else e = causal ? launch_bwd<128, true>(p, B, H, H_kv, s) : launch_bwd<128, false>(p, B, H, H_kv, s);
+  else if (d == 128) e = causal ? launch_bwd<128, true>(p, B, H, H_kv, s) : launch_bwd<128, false>(p, B, H, H_kv, s);
+  else e = causal ? launch_bwd<256, true>(p, B, H, H_kv, s) : launch_bwd<256, false>(p, B, H, H_kv, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -80,11 +80,13 @@ constexpr int kStatRows = 64;   // queries per statistics tile
 // the low field differs across any 4 consecutive rows of one bank phase (no
 // two transposed rows collide in a group of 4 chunks) and the whole value
 // is a bijection on 16 consecutive rows of one phase (row reads collide never).
+// Rows of 512 bytes (d = 256) span two bank spans; the XOR then acts on the
+// 16 chunk positions of one span exactly as for 256-byte rows.
 template <int CPR>
 __device__ __forceinline__ int swz_u(int row) {
-  static_assert(CPR == 8 || CPR == 16, "tile rows of 128 or 256 bytes");
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "tile rows of 128, 256 or 512 bytes");
   constexpr int RPP = CPR >= 16 ? 1 : 16 / CPR;
-  constexpr int A = CPR / 4;
+  constexpr int A = CPR >= 16 ? 4 : CPR / 4;
   const int rr = row / RPP;
   return 4 * (rr % A) + (rr / A) % 4;
 }
@@ -189,12 +191,13 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 // logical chunk) and transposed (8 consecutive rows x 2 adjacent chunks per
 // 32 lanes): with rr = row / RPP, XOR with 2 * (rr % (CPR/2)) + (rr / (CPR/2)) % 2,
 // a bijection on 16 consecutive rows of one bank phase whose upper bits
-// differ across 8 consecutive rows (4 per phase when two rows share a span).
+// differ across 8 consecutive rows (4 per phase when two rows share a span;
+// 512-byte rows XOR within the 16 positions of one span, as 256-byte rows do).
 template <int CPR>
 __device__ __forceinline__ int swz16(int row) {
-  static_assert(CPR == 8 || CPR == 16, "tile rows of 128 or 256 bytes");
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "tile rows of 128, 256 or 512 bytes");
   constexpr int RPP = CPR >= 16 ? 1 : 16 / CPR;
-  constexpr int A = CPR / 2;
+  constexpr int A = CPR >= 16 ? 8 : CPR / 2;
   const int rr = row / RPP;
   return 2 * (rr % A) + (rr / A) % 2;
 }
@@ -219,14 +222,18 @@ struct Stager16 {
   }
 };
 
-// A workgroup owns BK = 32*NW keys of one K/V head; wave w owns keys
-// 32w .. 32w+31 as two 16-key blocks.  K stays in VGPRs as B operands; V
-// (VLDS) is staged once into LDS and read as B operands, or kept in VGPRs.
-template <int D, int NW, int WPE, bool CAUSAL, bool VLDS>
+// A workgroup owns BK = KW*NW keys of one K/V head; wave w owns keys
+// KW*w .. KW*w + KW-1 as KW/16 blocks of 16 keys (KW = 32, or 16 at d = 256
+// to halve the registers K, V and the accumulators take).  K stays in VGPRs
+// as B operands; V (VLDS) is staged once into LDS and read as B operands, or
+// kept in VGPRs.
+template <int D, int NW, int WPE, bool CAUSAL, bool VLDS, int KW = 32>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(KW == 16 || KW == 32, "one or two 16-key blocks per wave");
+  constexpr int KBW = KW / 16;              // 16-key blocks per wave
   constexpr int BQ = kStatRows;             // queries per tile
-  constexpr int BK = 32 * NW;               // keys per workgroup
+  constexpr int BK = KW * NW;               // keys per workgroup
   constexpr int ROWB = 2 * D, CPR = ROWB / 16;
   constexpr int TILEB = BQ * ROWB;
   constexpr int STATB = 1024;               // L2 and D of the tile (512 B), then a copy
@@ -249,13 +256,13 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int bhk = vh / p.parts, hp = vh - bhk * p.parts;
   const int kblk = p.nrb - 1 - rb;          // causal: earliest key blocks (most query tiles) first
   const int N = p.N;
-  const int k0 = kblk * BK, kw0 = k0 + 32 * wave;
+  const int k0 = kblk * BK, kw0 = k0 + KW * wave;
   const int64_t kv_off = (int64_t)bhk * N * D;
 
   // K (and V) rows kw0 + 16*kb + m: chunk 4c + g of each row (zeros past N)
-  bf16x8 kf[2][NC], vf[2][VLDS ? 1 : NC];
+  bf16x8 kf[KBW][NC], vf[KBW][VLDS ? 1 : NC];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KBW; ++kb) {
     const int key = kw0 + 16 * kb + m;
     const bool ok = key < N;
     const i32x4* ks = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.k) + kv_off + (int64_t)key * D);
@@ -267,9 +274,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  f32x4 dk[2][NDB], dv[2][NDB];
+  f32x4 dk[KBW][NDB], dv[KBW][NDB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
     for (int b = 0; b < NDB; ++b) dk[kb][b] = dv[kb][b] = f32x4{};
 
@@ -302,10 +309,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const i16x4 lo = lds_tr16(base + off0), hi = lds_tr16(base + off1);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // B operand V^T: keys 32*wave + 16*kb + m, dims 32c + 8g .. +7
+  // B operand V^T: keys KW*wave + 16*kb + m, dims 32c + 8g .. +7
   auto v_b = [&](int kb, int c) __attribute__((always_inline)) {
     if constexpr (VLDS) {
-      const int row = 32 * wave + 16 * kb + m;
+      const int row = KW * wave + 16 * kb + m;
       return __builtin_bit_cast(bf16x8, lds_read16(vsm + row * ROWB + (((4 * c + g) ^ swz16<CPR>(row)) << 4)));
     } else {
       return vf[kb][c];
@@ -319,41 +326,43 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     if (CAUSAL && qt0 + BQ - 1 < kw0) return;          // every query of the tile precedes every key of the wave
     const char FA_LDS* dos = qs + TILEB;
     const char FA_LDS* st = qs + 2 * TILEB;
-    const bool diag = CAUSAL && qt0 < kw0 + 31;
+    const bool diag = CAUSAL && qt0 < kw0 + KW - 1;
     const int lim = kw0 + m - qt0 - 4 * g;              // keep element iff its (query - key) offset >= lim
 #pragma unroll
     for (int s = 0; s < BQ / 32; ++s) {
-      i32x4 pp[2], dsp[2];                              // B operands of this 32-query step, per key block
+      i32x4 pp[KBW], dsp[KBW];                          // B operands of this 32-query step, per key block
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int qb = 2 * s + h;
-        f32x4 sc[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
+        f32x4 sc[KBW], dp[KBW];
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) sc[kb] = dp[kb] = f32x4{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const bf16x8 aq = row_a(qs, qb, c);
           const bf16x8 ao = row_a(dos, qb, c);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
+          for (int kb = 0; kb < KBW; ++kb) {
             sc[kb] = mfma16(aq, kf[kb][c], sc[kb]);
             dp[kb] = mfma16(ao, v_b(kb, c), dp[kb]);
           }
         }
         const f32x4 l2 = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * (16 * qb + 4 * g));
         const f32x4 dd = *reinterpret_cast<const f32x4 FA_LDS*>(st + 4 * (kStatRows + 16 * qb + 4 * g));
-        float pr[2][4];
+        float pr[KBW][4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) pr[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][j], c2, -l2[j]));
         if (diag) {
           asm volatile("" ::: "memory");                // keep this a branch: only diagonal tiles mask
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) pr[kb][j] = (16 * qb + j - 16 * kb) >= lim ? pr[kb][j] : 0.f;
         }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
           float ds[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) ds[j] = pr[kb][j] * (dp[kb][j] - dd[j]);
@@ -368,7 +377,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const bf16x8 ao = tr_a(dos, s, db);
         const bf16x8 aq = tr_a(qs, s, db);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KBW; ++kb) {
           dv[kb][db] = mfma16(ao, __builtin_bit_cast(bf16x8, pp[kb]), dv[kb][db]);
           dk[kb][db] = mfma16(aq, __builtin_bit_cast(bf16x8, dsp[kb]), dk[kb][db]);
         }
@@ -419,7 +428,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     dv_base = p.part_out + (p.parts + hp) * slab;
   }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KBW; ++kb) {
     const int key = kw0 + 16 * kb + m;
     if (key < N) {
       float* dkp = dk_base + kv_off + (int64_t)key * D + 4 * g;

@@ -65,7 +65,7 @@ fa_status fa_bwd_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t N, i
  *   dq        : output, float32 [B][H][N][d]
  *   dk, dv    : outputs, float32 [B][H_kv][N][d] (each K/V head's sum over its group)
  *   H_kv      : K/V heads, >= 1 and dividing H (H_kv = H: one K/V head per head)
- *   d         : 64 or 128, else FA_ERR_UNSUPPORTED
+ *   d         : 64, 128 or 256, else FA_ERR_UNSUPPORTED
  *   scale     : finite, the value the forward used
  *   causal    : 0 = no mask, nonzero = query i sees keys j <= i (as in the forward)
  * Every pointer must be 16-byte aligned (FA_ERR_ALIGN).  The statistics D are

@@ -134,7 +134,9 @@ def test_fa_bwd_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(0, 1, 1, 64, 64, ctypes.byref(n)) == 2
     assert lib.fa_bwd_workspace_size(1, 1, 1, 0, 64, ctypes.byref(n)) == 2
     assert lib.fa_bwd_workspace_size(1, 8, 3, 64, 64, ctypes.byref(n)) == 2
-    assert lib.fa_bwd_workspace_size(1, 1, 1, 64, 256, ctypes.byref(n)) == 3
+    assert lib.fa_bwd_workspace_size(1, 1, 1, 64, 96, ctypes.byref(n)) == 3
+    # d = 256: the same statistics; partials scale with d
+    assert lib.fa_bwd_workspace_size(1, 8, 2, 64, 256, ctypes.byref(n)) == 0 and n.value == 8 * 512 + 2 * 8 * 64 * 256 * 4
 
 
 def _bwd_args(**kw):
@@ -149,7 +151,7 @@ def _bwd_args(**kw):
     ({"q": 0}, 1), ({"do": 0}, 1), ({"lse": 0}, 1), ({"ws": 0}, 1), ({"dv": 0}, 1),
     ({"B": 0}, 2), ({"N": 0}, 2), ({"H_kv": 0}, 2), ({"H_kv": 3}, 2), ({"H": 2, "H_kv": 4}, 2),
     ({"N": 2**40}, 2), ({"B": 2**31, "H": 2**31}, 2),
-    ({"d": 256}, 3), ({"d": 96}, 3), ({"dtype": 0}, 3), ({"dtype": 2}, 3),
+    ({"d": 512}, 3), ({"d": 96}, 3), ({"dtype": 0}, 3), ({"dtype": 2}, 3),
     ({"o": FAKE + 8}, 4), ({"ws": FAKE + 4}, 4), ({"dk": FAKE + 2}, 4),
     ({"scale": float("inf")}, 5), ({"scale": float("nan")}, 5), ({"scale": 3e38}, 5),
 ])

@@ -54,7 +54,8 @@ def modelled_head(q, k, v, do, scale, causal, rounded=True):
 
 # (N, d, causal, scale, bound the GPU tests hold the gradients to)
 CASES = [(333, 64, True, None, 5e-3), (1000, 128, True, None, 5e-3), (700, 128, False, None, 5e-3),
-         (200, 64, True, 0.9, 1e-2), (200, 128, True, 0.9, 1e-2), (200, 128, True, -0.3, 5e-3)]
+         (200, 64, True, 0.9, 1e-2), (200, 128, True, 0.9, 1e-2), (200, 128, True, -0.3, 5e-3),
+         (333, 256, True, None, 5e-3), (300, 256, False, None, 5e-3), (200, 256, True, 0.9, 1e-2)]
 
 
 def _head_inputs(N, d, causal):

@@ -98,6 +98,10 @@ REDUCED_BWD = [
     (1, 4, 1, 257, 64, False),     # one K/V head for all query heads
     (2, 6, 3, 200, 128, True),
     (1, 16, 8, 129, 64, True),     # 8 K/V heads: one per XCD
+    (1, 2, 2, 333, 256, True),     # d = 256: 16 keys per dK/dV wave, 32-key dQ tiles
+    (2, 2, 2, 300, 256, False),
+    (1, 8, 2, 300, 256, True),
+    (1, 4, 1, 257, 256, False),
 ]
 
 
@@ -111,7 +115,7 @@ def test_backward_reduced_all_elements(B, H, H_kv, N, d, causal):
     check_grads(run_bwd(x, do, o, l), oracle_bwd(x, do), f"B={B} H={H} H_kv={H_kv} N={N} d={d} causal={causal}")
 
 
-EDGE_BWD = [(N, d, c) for d in (64, 128) for N in (1, 7, 64, 65, 100, 257) for c in (False, True)]
+EDGE_BWD = [(N, d, c) for d in (64, 128, 256) for N in (1, 7, 64, 65, 100, 257) for c in (False, True)]
 
 
 @pytest.mark.parametrize("N,d,causal", EDGE_BWD)
@@ -125,7 +129,7 @@ def test_backward_edge_shapes(N, d, causal):
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 0.9])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_backward_other_scales(scale, d):
     """Negative, zero and large scales.  At |scale| * sqrt(d) > 3 the softmax rows
     are close to one-hot and the bf16 rounding of dS dominates: the float64
@@ -179,7 +183,7 @@ def test_backward_is_bitwise_reproducible():
 
 # ---------------------------------------------------------------- forward then backward on the GPU
 @pytest.mark.parametrize("B,H,H_kv,N,d,causal", [(1, 2, 2, 1000, 128, True), (1, 8, 2, 333, 64, True),
-                                                 (2, 2, 2, 500, 64, False)])
+                                                 (2, 2, 2, 500, 64, False), (1, 4, 2, 700, 256, True)])
 def test_forward_then_backward(B, H, H_kv, N, d, causal):
     _print_case("fwd+bwd", B, H, H_kv, N, d, causal)
     w = _case(B, H, H_kv, N, d, causal, seed=31)
@@ -224,11 +228,13 @@ def test_backward_full_bertl_all_elements():
     check_grads(run_bwd(x, do, o, l), oracle_bwd(x, do), w.name)
 
 
-@pytest.mark.parametrize("name,heads", [("long_causal_bf16_b1h32n8192d128", (0, 31)),
-                                        ("gqa_causal_bf16_b1h32kv8n8192d128", (5,))])
+@pytest.mark.parametrize("name,heads", [("long_causal_bf16_b1h32n8192d128", ((0, 0), (0, 31))),
+                                        ("gqa_causal_bf16_b1h32kv8n8192d128", ((0, 5),)),
+                                        ("wide_bf16_b2h8n16384d256", ((0, 0), (1, 7)))])
 def test_backward_full_sampled(name, heads):
-    """Full-size long-context cases: dQ on sampled query rows, dK and dV on
-    sampled keys of sampled K/V heads (each K/V key summed over its group)."""
+    """Full-size long-context and d = 256 cases: dQ on sampled query rows, dK
+    and dV on sampled keys of sampled (batch, K/V head) pairs (each K/V key
+    summed over its group)."""
     w = by_name(name)
     _print_case("full-sampled", name)
     x = make_inputs(w)
@@ -240,17 +246,17 @@ def test_backward_full_sampled(name, heads):
     edges = np.array([0, 1, 63, 64, 127, 128, 255, 256, w.N // 2, w.N - 2, w.N - 1])
     rows = np.unique(np.concatenate([edges, rng.choice(w.N, 24, replace=False)]))
     do64 = bf16_bits_to_f64(do)
-    for g in heads:
-        kk, vv = x.f64("k", 0, g), x.f64("v", 0, g)
+    for b, g in heads:
+        kk, vv = x.f64("k", b, g), x.f64("v", b, g)
         ref_dk = np.zeros((len(rows), w.d))
         ref_dv = np.zeros_like(ref_dk)
         for h in range(g * G, (g + 1) * G):
-            qq = x.f64("q", 0, h)
-            ref_dq = dq_rows(qq, kk, vv, do64[0, h], sc, w.causal, rows)
-            check_grads((dq[0, h, rows],), (ref_dq,), f"{name} dq head {h}")
-            a, b = dkdv_cols(qq, kk, vv, do64[0, h], sc, w.causal, rows)
+            qq = x.f64("q", b, h)
+            ref_dq = dq_rows(qq, kk, vv, do64[b, h], sc, w.causal, rows)
+            check_grads((dq[b, h, rows],), (ref_dq,), f"{name} dq batch {b} head {h}")
+            a, c = dkdv_cols(qq, kk, vv, do64[b, h], sc, w.causal, rows)
             ref_dk += a
-            ref_dv += b
+            ref_dv += c
         # check_grads names its pairs dq, dk, dv in order: pass a placeholder first
-        check_grads((ref_dq[:0], dk[0, g, rows], dv[0, g, rows]), (ref_dq[:0], ref_dk, ref_dv),
-                    f"{name} K/V head {g}")
+        check_grads((ref_dq[:0], dk[b, g, rows], dv[b, g, rows]), (ref_dq[:0], ref_dk, ref_dv),
+                    f"{name} batch {b} K/V head {g}")
