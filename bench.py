@@ -76,7 +76,9 @@ HBM_GBPS = 8000.0
 # forward workloads whose inputs fit in the 256 MiB MALL: also timed cold
 COLD_WORKLOADS = ["gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64"]
 BWD_WORKLOADS = ["long_causal_bf16_b1h32n8192d128", "gqa_causal_bf16_b1h32kv8n8192d128",
-                 "gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64"]
+                 "gpt2s_causal_bf16_b8h12n1024d64", "bertl_bf16_b16h16n512d64", "wide_bf16_b2h8n16384d256"]
+# forward workloads also timed with ALiBi biases
+ALIBI_WORKLOADS = ["long_causal_bf16_b1h32n8192d128", "gpt2s_causal_bf16_b8h12n1024d64", "wide_fp8_b2h8n16384d256"]
 KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_tile.hpp",
                   "exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp", "exact_io_aware_48_amd/csrc/fa_pipe_kernel.hpp",
                   "exact_io_aware_48_amd/csrc/fa_host.hpp", "exact_io_aware_48_amd/csrc/fa_launch.hpp",
@@ -196,10 +198,16 @@ def alibi_slopes(H):
 def time_alibi(w, steps, warmup, settle_s=0.25, graph=False):
     import torch
     import exact_io_aware_48_amd as fa
-    _, q, k, v = device_inputs(w)
+    x, q, k, v = device_inputs(w)
     slopes = torch.tensor(alibi_slopes(w.H), dtype=torch.float32, device="cuda")
-    o, lse = torch.empty_like(q), torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
-    launch = lambda: fa.fa_fwd_alibi(q, k, v, slopes, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    if w.dtype == "fp8":
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+        launch = lambda: fa.fa_fwd_alibi_fp8(q, k, v, slopes, *x.descale, o=o, lse=lse, scale=w.softmax_scale,
+                                             causal=w.causal)
+    else:
+        o = torch.empty_like(q)
+        launch = lambda: fa.fa_fwd_alibi(q, k, v, slopes, o=o, lse=lse, scale=w.softmax_scale, causal=w.causal)
     return time_launch(launch, steps, warmup, settle_s, graph)
 
 
@@ -729,12 +737,12 @@ def main():
         line["backward"] = bwd
     if not args.no_variants:
         var = {}
-        for name in ("long_causal_bf16_b1h32n8192d128", "gpt2s_causal_bf16_b8h12n1024d64"):
+        for name in ALIBI_WORKLOADS:
             vw = by_name(name)
             at = time_alibi(vw, None, max(3, args.warmup // 2), args.settle, graph=args.graph)
             tf = vw.flops / (at["kernel_ms_mean"] * 1e-3) / 1e12
             var["alibi:" + name] = {"ms_per_call": round(at["kernel_ms_mean"], 4), "tflops": round(tf, 1),
-                                    "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS["bf16"], 2)}
+                                    "pct_of_dense_peak": round(100 * tf / PEAK_TFLOPS[vw.dtype], 2)}
         sw = by_name("long_causal_bf16_b1h32n8192d128").with_(causal=False)
         bm = local_global_mask(sw.N)
         bt = time_blocksparse(sw, bm, None, max(3, args.warmup // 2), args.settle,
