@@ -53,8 +53,9 @@
 //   MODE_BF16 : bf16 in/out, v_mfma_f32_32x32x16_bf16 for both products.
 //   MODE_FP8  : OCP e4m3fn in (per-tensor descales), bf16 out,
 //               v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) for both
-//               products; P is rounded to e4m3 as 256 * P (the exponentials
-//               produce it directly: the factor is in their base).
+//               products; P is rounded to e4m3 as 2^6 * P, at most 2^8
+//               with the rescale lag of 2 (the exponentials produce it
+//               directly: the factor is in their base).
 //   MODE_F32  : fp32 in/out; each operand x is split as hi = bf16(x),
 //               lo = bf16(x - hi) and each product uses hi*hi + hi*lo + lo*hi.
 #pragma once

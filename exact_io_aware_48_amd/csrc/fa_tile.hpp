@@ -26,13 +26,17 @@ struct Tile {
   static constexpr int NDB = D / 32;                                // 32-wide blocks of the head dim
   static constexpr int QK_STEPS = MODE == MODE_FP8 ? D / 64 : D / 16;   // MFMA k-steps over d
   static constexpr int PV_STEPS = MODE == MODE_FP8 ? BC / 64 : BC / 16; // MFMA k-steps over keys
-  // lazy-rescale threshold (log2 units); fp8 keeps P <= 1 so that 256 * P fits e4m3
-  static constexpr float TAU = MODE == MODE_FP8 ? 0.f : 8.f;
-  // fp8: P is stored as e4m3 of 256 * P (2^8 keeps small probabilities out of
-  // e4m3's subnormal range); the factor is taken into the exponent base, so
-  // the exponentials produce 256 * P directly and l sums 256 * P as well.  O
-  // is unchanged (the factor cancels in O / l) and L subtracts it back.
-  static constexpr float EXP_SHIFT = MODE == MODE_FP8 ? 8.f : 0.f;
+  // Lazy-rescale threshold (log2 units): the exponent base may lag a row's
+  // running max by up to TAU, so P <= 2^TAU.  fp8 stores P as e4m3 of
+  // 2^EXP_SHIFT * P <= 2^8 (e4m3 holds up to 448); the pre-scale keeps small
+  // probabilities out of e4m3's subnormal range (normal down to P = 2^-12).
+  // A lag of 2 instead of 0 removes most of the O rescales (128 multiplies
+  // each at d = 256), which fp8's short MFMA time does not hide.  The factor
+  // is taken into the exponent base, so the exponentials produce the scaled P
+  // directly and l sums it as well; O is unchanged (the factor cancels in
+  // O / l) and L subtracts it back.
+  static constexpr float TAU = MODE == MODE_FP8 ? 2.f : 8.f;
+  static constexpr float EXP_SHIFT = MODE == MODE_FP8 ? 8.f - TAU : 0.f;
 
   // the wave's 32 queries as the B operand of S^T = K Q^T
   struct QFrag {
@@ -42,7 +46,7 @@ struct Tile {
   };
   // P of one tile as the B operand of O^T += V^T P^T
   //   bf16/fp32: element i of step s <- key 16*s + 8*(i/4) + 4*hf + i%4 (hi parts; lo in l)
-  //   fp8:       byte 16*kb' + i of step g <- key 64*g + 32*kb' + 8*(i/4) + 4*hf + i%4, x256
+  //   fp8:       byte 16*kb' + i of step g <- key 64*g + 32*kb' + 8*(i/4) + 4*hf + i%4, x 2^EXP_SHIFT
   struct PFrag {
     i32x4 h[MODE == MODE_FP8 ? 1 : PV_STEPS];    // bf16 pairs
     i32x4 l[MODE == MODE_F32 ? PV_STEPS : 1];
