@@ -174,6 +174,61 @@ def test_running_max_grows_at_row_dependent_rates(dtype, d, causal):
     check(errors(o, ref, l, lref), dtype, f"row-dependent growth {dtype} d={d} causal={causal}")
 
 
+# ---------------------------------------------------------------- maximum sizes
+def _edge_rows(N, extra, seed):
+    rng = np.random.default_rng(seed)
+    edges = [0, 1, 63, 64, 255, 256, N // 2, N - 257, N - 256, N - 2, N - 1]
+    return np.unique(np.concatenate([edges, rng.choice(N, extra, replace=False)])).astype(np.int64)
+
+
+def test_long_context_n131072_sampled_rows():
+    """N = 131072 keys, causal, d = 128 (the largest context the tests run):
+    seeded inputs, sampled rows of both heads against the float64 oracle."""
+    w = by_name("long_causal_bf16_b1h32n8192d128").with_(H=2, N=131072, seed=131)
+    _print_case("long-context", w.N)
+    x = make_inputs(w)
+    o, l = run_gpu(x)
+    rows = _edge_rows(w.N, 40, 5)
+    for h in range(2):
+        o_ref, l_ref = attention_rows(x.f64("q", 0, h), x.f64("k", 0, h), x.f64("v", 0, h), w.softmax_scale, True,
+                                      rows)
+        check(errors(o[0, h, rows], o_ref, l[0, h, rows], l_ref), "bf16", f"N=131072 head {h}")
+
+
+def test_offsets_beyond_2_31_elements():
+    """B=1, H=72, N=131072, d=256 (2.4e9 elements per tensor, 4.5 GiB each):
+    head 64 starts exactly at element 2^31 and the later heads past it.  Q = 0 makes every score 0, so query i
+    sees its visible keys uniformly: O_i is the mean of V over keys j <= i and
+    L_i = log(i + 1) (a property that holds at any size).  V is a pattern with
+    values k/16, k = (7j + 3c + 5h) mod 17, exact in bf16, built on the device;
+    sampled rows of sampled heads are compared with the float64 prefix means."""
+    import exact_io_aware_48_amd as fa
+    B, H, N, d = 1, 72, 131072, 256
+    assert 64 * N * d == 2**31
+    _print_case("offsets>2^31", B, H, N, d)
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros_like(q)
+    v = torch.empty_like(q)
+    j = torch.arange(N, device="cuda", dtype=torch.int64)[:, None]
+    c = torch.arange(d, device="cuda", dtype=torch.int64)[None, :]
+    for h in range(H):
+        v[0, h] = (((7 * j + 3 * c + 5 * h) % 17).to(torch.float32) / 16).to(torch.bfloat16)
+    del j, c
+    o, lse = fa.fa_fwd(q, k, v, scale=1.0 / 16, causal=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    rows = _edge_rows(N, 24, 6)
+    rows_t = torch.from_numpy(rows).cuda()
+    jj = np.arange(N, dtype=np.int64)[:, None]
+    cc = np.arange(d, dtype=np.int64)[None, :]
+    for h in (0, 40, 63, 64, 71):
+        got_o = o[0, h].index_select(0, rows_t).float().cpu().numpy().astype(np.float64)
+        got_l = lse[0, h].index_select(0, rows_t).cpu().numpy().astype(np.float64)
+        vals = ((7 * jj + 3 * cc + 5 * h) % 17).astype(np.float64) / 16
+        prefix = np.cumsum(vals, axis=0)[rows] / (rows[:, None] + 1)
+        check(errors(got_o, prefix, got_l, np.log(rows + 1.0)), "bf16", f"offsets>2^31 head {h}")
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
 def test_other_scales(scale):
     w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=2, N=190, d=64, causal=True)
