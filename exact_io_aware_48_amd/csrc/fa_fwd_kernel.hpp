@@ -35,12 +35,14 @@
 //     idle).  The upper half of the waves therefore runs each tile's P V one
 //     iteration late -- [P V_{j-1}] [S_j, softmax_j] against the lower half's
 //     [S_j, softmax_j] [P V_j] -- so one wave's softmax overlaps the other's
-//     MFMAs.  The V ring keeps one extra tile for the late group.
+//     MFMAs.  The V ring keeps one extra tile for the late group.  (An
+//     option: raised wave priority outside the MFMA blocks measured faster
+//     on every shape, so no instance uses ping-pong now.)
 //   * The grid is mapped so that all row blocks of a head run on one XCD
 //     (workgroups are dealt to the 8 XCDs round-robin), keeping that head's
 //     K/V stream in one L2.
 //
-// Variants (bf16, PP off):
+// Variants (every mode, PP off):
 //   VAR_ALIBI       : the score of query i and key j gets -slope_h * |i - j|
 //                     after scaling (added to the unscaled score as
 //                     -slope_h / |scale| * |i - j| before the softmax).

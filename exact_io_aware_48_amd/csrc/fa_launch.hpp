@@ -28,9 +28,11 @@ struct Tile {
 // workgroup (256 query rows) halve the K/V traffic per FLOP for the large
 // heads; d = 64 keeps four waves so that the short causal rows spread over
 // more workgroups.  d = 256 with 16-bit tiles uses 32-key tiles to stay
-// within 256 VGPRs at two waves per SIMD.  PP: ping-pong wave groups (the
-// upper half of the waves runs P V one tile late), which pays off for fp8.
-// PRIO: raised wave priority outside the MFMA blocks (d = 256 bf16).
+// within 256 VGPRs at two waves per SIMD.  PRIO: raised wave priority
+// outside the MFMA blocks (bf16 d = 256; fp8 d = 128 and 256, where it beat
+// ping-pong by 2.1% and 1.4%).  PP: ping-pong wave groups (the upper half of
+// the waves runs P V one tile late); the kernel keeps the option, no shape
+// uses it since.
 // PIPE: the software-pipelined kernel (fa_pipe_kernel.hpp), whose waves weave
 // each tile's softmax into the neighbouring tiles' MFMAs (bf16, d = 128).
 template <int MODE, int D> struct Cfg;
@@ -42,20 +44,17 @@ template <> struct Cfg<fa::MODE_BF16, 64> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_BF16, 128> : Shape<64, 8, false, false, true> {};
 template <> struct Cfg<fa::MODE_BF16, 256> : Shape<32, 8, false, true> {};
 template <> struct Cfg<fa::MODE_FP8, 64> : Shape<64, 4, false> {};
-template <> struct Cfg<fa::MODE_FP8, 128> : Shape<64, 8, true> {};
-template <> struct Cfg<fa::MODE_FP8, 256> : Shape<64, 8, true> {};
+template <> struct Cfg<fa::MODE_FP8, 128> : Shape<64, 8, false, true> {};
+template <> struct Cfg<fa::MODE_FP8, 256> : Shape<64, 8, false, true> {};
 template <> struct Cfg<fa::MODE_F32, 64> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_F32, 128> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_F32, 256> : Shape<32, 4, false> {};
 // The ALiBi and block-sparse variants are instances of fa_fwd_kernel with
 // the plain shape's row block (so the grid is the same): bf16 d = 128 keeps
-// the 128-key tiles measured for it before the pipelined kernel; fp8 runs
-// without ping-pong (its late wave group would need the bias and the mask
-// one tile later); raised priority is for the plain kernel only.
+// the 128-key tiles measured for it before the pipelined kernel; raised
+// priority is for the plain kernel only.
 template <int MODE, int D> struct VarCfg : Cfg<MODE, D> {};
 template <> struct VarCfg<fa::MODE_BF16, 128> : Shape<128, 8, false> {};
-template <> struct VarCfg<fa::MODE_FP8, 128> : Shape<64, 8, false> {};
-template <> struct VarCfg<fa::MODE_FP8, 256> : Shape<64, 8, false> {};
 
 template <int MODE, int D>
 Tile tile_for() {

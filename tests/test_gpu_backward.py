@@ -228,6 +228,32 @@ def test_backward_full_bertl_all_elements():
     check_grads(run_bwd(x, do, o, l), oracle_bwd(x, do), w.name)
 
 
+def test_backward_long_context_n32768_sampled():
+    """N = 32768, causal, d = 128, two query heads over one K/V head: dQ on
+    sampled query rows and dK, dV on sampled keys (summed over the group)."""
+    w = _case(1, 2, 1, 32768, 128, True, seed=327)
+    _print_case("long-context", w.N)
+    x = make_inputs(w)
+    do = make_grad_output(w)
+    o, l = _fwd_from_gpu(x)
+    dq, dk, dv = run_bwd(x, do, o, l)
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, w.N // 2, w.N - 2, w.N - 1],
+                                     rng.choice(w.N, 12, replace=False)]))
+    do64 = bf16_bits_to_f64(do)
+    kk, vv = x.f64("k", 0, 0), x.f64("v", 0, 0)
+    ref_dk = np.zeros((len(rows), w.d))
+    ref_dv = np.zeros_like(ref_dk)
+    for h in range(2):
+        qq = x.f64("q", 0, h)
+        ref_dq = dq_rows(qq, kk, vv, do64[0, h], w.softmax_scale, True, rows)
+        check_grads((dq[0, h, rows],), (ref_dq,), f"N=32768 dq head {h}")
+        a, b = dkdv_cols(qq, kk, vv, do64[0, h], w.softmax_scale, True, rows)
+        ref_dk += a
+        ref_dv += b
+    check_grads((ref_dq[:0], dk[0, 0, rows], dv[0, 0, rows]), (ref_dq[:0], ref_dk, ref_dv), "N=32768 K/V head 0")
+
+
 @pytest.mark.parametrize("name,heads", [("long_causal_bf16_b1h32n8192d128", ((0, 0), (0, 31))),
                                         ("gqa_causal_bf16_b1h32kv8n8192d128", ((0, 5),)),
                                         ("wide_bf16_b2h8n16384d256", ((0, 0), (1, 7)))])
