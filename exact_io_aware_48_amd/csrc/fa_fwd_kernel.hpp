@@ -183,15 +183,17 @@ void fa_fwd_kernel(Params p) {
   float alibi_a = 0.f;
   if constexpr (VAR == VAR_ALIBI) alibi_a = p.slopes[bh % p.H] * p.alibi_mul;
 
-  // S_j = K_j Q^T, online-softmax update, P_j packed into pf
-  auto qk_softmax = [&](int j, const char FA_LDS* kbase) __attribute__((always_inline)) {
-    f32x16 st[T::KB];
+  // S_j = K_j Q^T (+ ALiBi bias, masks) into st
+  auto scores = [&](int j, const char FA_LDS* kbase, f32x16 (&st)[T::KB]) __attribute__((always_inline)) {
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     T::qk(st, kbase, q, ln);
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     const int key0 = j * BC;
     if constexpr (VAR == VAR_ALIBI) T::alibi(st, (float)(my_q - key0 - 4 * ln.hf), alibi_a);
     if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > qw0)) T::mask(st, last_key - key0);
+  };
+  // the max-first online-softmax update of st (raw scores), P packed into pf
+  auto softmax_max_first = [&](f32x16 (&st)[T::KB]) __attribute__((always_inline)) {
     typename T::Softmax sm;
     T::template softmax_slices<0, T::NMAX + 1>(st, sm, m_run, c2, pf);
     if (__builtin_amdgcn_ballot_w64(sm.grow)) {
@@ -202,6 +204,38 @@ void fa_fwd_kernel(Params p) {
     }
     T::template softmax_slices<T::NMAX + 1, T::NSLICES>(st, sm, m_run, c2, pf);
     l_run += sm.psum[0] + sm.psum[1];
+  };
+  // S_j, online-softmax update, P_j packed into pf
+  auto qk_softmax = [&](int j, const char FA_LDS* kbase) __attribute__((always_inline)) {
+    f32x16 st[T::KB];
+    scores(j, kbase, st);
+    if constexpr (T::SPEC && VAR == VAR_NONE) {
+      // Once every row of the wave has a base, the exponentials are taken
+      // against it without the row max (Tile::SPEC).  The max-first order
+      // (Tile::rebase) runs for a wave with a row that has no base yet, and
+      // again for a tile whose lane sum passed 2^TAU, with its scores
+      // recomputed from the K tile (in LDS until the barrier ending the step).
+      bool max_first = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
+      float alpha = 1.f, psum;
+      for (;;) {
+        T::to_exponents(st, c2, m_run == -INFINITY ? 0.f : m_run);
+        if (max_first) alpha = T::rebase(st, m_run);
+        psum = T::probs(st, pf);
+        if (max_first || !__builtin_amdgcn_ballot_w64(!(psum <= T::TAU_P))) break;
+        asm volatile("" ::: "memory");   // a real (rarely taken) branch
+        max_first = true;
+        scores(j, kbase, st);
+      }
+      if (max_first) {
+        asm volatile("" ::: "memory");
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+      }
+      l_run += psum;
+    } else {
+      softmax_max_first(st);
+    }
   };
   auto pv = [&](const char FA_LDS* vbase) __attribute__((always_inline)) {
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);

@@ -23,20 +23,24 @@
 //   iteration j:  stage A  S_{j+1} = K_{j+1} Q^T        (16 MFMAs at d=128)
 //                          with the exponentials, bf16 packing and row sums
 //                          of tile j woven in (exp2(x), x = c2*s - m, the
-//                          running max already subtracted)
+//                          exponent base already subtracted)
+//                 [if some lane's sum of tile j's probabilities passed
+//                  2^TAU: tile j's row max, new bases where a row grew by
+//                  more than TAU, tile j's probabilities again, O and l
+//                  *= alpha -- rare once the bases have settled]
 //                 stage B  O^T += V_j^T P_j^T            (16 MFMAs at d=128)
-//                          with the row max of S_{j+1}, the rescale decision
-//                          and x = c2*s - m for tile j+1 woven in
-//                 [O and l *= alpha when a row's max grew past the lag limit]
+//                          with x = c2*s - m for tile j+1 woven in, against
+//                          the base in use (no row max: see Tile::SPEC)
 //
 // The order inside each stage (one MFMA, its LDS operand reads run three
 // items ahead, then a fixed number of VALU and transcendental instructions)
 // is pinned with sched_group_barrier.  Dependencies stay exact: tile j's
-// exponentials use the base fixed when tile j's max was taken (stage B of
-// iteration j-1), P_j V_j is added under that base, and the rescale for tile
-// j+1's max multiplies O and l after P_j V_j has been added and before tile
-// j+1's probabilities are.  The result is the same as fa_fwd_kernel's up to
-// the order of floating-point additions.
+// exponentials use the base in use when its exponents were formed (stage B
+// of iteration j-1); a base that moves for tile j moves before P_j V_j is
+// added, with O and l rescaled first.  Tile 0's base is its row max.  Bases,
+// probabilities and rescales are those of taking every tile's row max first
+// under the lazy rule; the result is the same as fa_fwd_kernel's up to the
+// order of floating-point additions.
 //
 // K/V stream: 64-key tiles through two-slot K and V rings in LDS
 // (global_load_lds_dwordx4, XOR-swizzled as in fa_tile.hpp).  Iteration j
@@ -88,11 +92,6 @@ struct PipeWave {
   static constexpr float TAU = T::TAU;
   using Op = typename T::Op;
 
-  struct Stats {
-    float alpha;     // factor for O and l (1 when the base is kept)
-    bool grow;       // this lane's base moved
-  };
-
   // ---- stage A work: tile j's exponentials (x already holds c2*s - m), P_j
   // packed as the MFMA B operand, and this lane half's sum of the fp32
   // probabilities, in QK_NI slices of NS / 2 / QK_NI score pairs each (per
@@ -123,58 +122,6 @@ struct PipeWave {
 #pragma unroll
     for (int pr = 0; pr < NS / 2; ++pr) prob_pair(pr, x, pf, ps);
     psum = ps.sum0 + ps.sum1;
-  }
-
-  // ---- stage B work: tile j+1's row max, the lagged base (m_run) and the
-  // factor for O and l, then x = c2 * s - m_use in place, in PV_NI slices:
-  //   slices 0 .. NMAX-1   the maximum of 8 scores each (v_maximum3 chains)
-  //   slice NMAX           the row max over both lane halves, the base and alpha
-  //   the remaining        x = c2 * s - m_use, an even share of the scores each
-  // real = false: s holds no tile (a wave's last step computes a throwaway
-  // product); m_run stays and grow is false.
-  static constexpr int NMAX = NS / 8;
-  static constexpr int FMA_SLOTS = PV_NI - NMAX - 1;
-  static_assert(FMA_SLOTS >= 1, "room for the scale-subtract");
-  struct MaxState {
-    float m8[NMAX];
-    float m_use;
-  };
-  template <int SL>
-  static __device__ __forceinline__ void max_slice(f32x16 (&s)[KB], float c2, float& m_run, Stats& st, MaxState& ms,
-                                                   bool real) {
-    if constexpr (SL < NMAX) {
-      const int kb = SL / 2, i0 = 8 * (SL % 2);
-      float m = s[kb][i0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) m = __builtin_elementwise_maximum(m, s[kb][i0 + i]);
-      ms.m8[SL] = m;
-    } else if constexpr (SL == NMAX) {
-      float m = ms.m8[0];
-#pragma unroll
-      for (int i = 1; i < NMAX; ++i) m = __builtin_elementwise_maximum(m, ms.m8[i]);
-      const float m_tile = swap_halves_max(m) * c2;
-      st.grow = real && m_tile > m_run + TAU;
-      st.alpha = st.grow ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.f;
-      m_run = st.grow ? m_tile : m_run;
-      ms.m_use = m_run == -INFINITY ? 0.f : m_run;
-    } else {
-      constexpr int f = SL - NMAX - 1;
-      constexpr int v0 = f * NS / FMA_SLOTS, v1 = (f + 1) * NS / FMA_SLOTS;
-#pragma unroll
-      for (int v = v0; v < v1; ++v) s[v / 16][v % 16] = __builtin_fmaf(s[v / 16][v % 16], c2, -ms.m_use);
-    }
-  }
-  // the whole tile at once (outside the pipeline)
-  static __device__ __forceinline__ void scores_to_exponents(f32x16 (&s)[KB], float c2, float& m_run, Stats& st) {
-    MaxState ms;
-    max_all<0>(s, c2, m_run, st, ms);
-  }
-  template <int SL>
-  static __device__ __forceinline__ void max_all(f32x16 (&s)[KB], float c2, float& m_run, Stats& st, MaxState& ms) {
-    if constexpr (SL < PV_NI) {
-      max_slice<SL>(s, c2, m_run, st, ms, true);
-      max_all<SL + 1>(s, c2, m_run, st, ms);
-    }
   }
 
   // Empty asm uses keep a stage's results in the stage's own block: without
@@ -214,15 +161,22 @@ struct PipeWave {
     anchor_p(pf, psum);
   }
 
-  // stage B: O^T += V^T P^T over the tile at vbase, with nxt's max and exponents woven in
+  // stage B: O^T += V^T P^T over the tile at vbase, with nxt's exponents
+  // x = c2 * s - m_run woven in (against the base in use: no row max)
+  static constexpr int X_PER_SLOT = NS / PV_NI;
+  static_assert(X_PER_SLOT * PV_NI == NS, "scores split evenly over the P V MFMAs");
   static __device__ __forceinline__ void stage_b(f32x16 (&oacc)[NDB], const char FA_LDS* vbase,
                                                  const typename T::PFrag& pf, const typename T::Lane& ln,
-                                                 f32x16 (&nxt)[KB], float c2, float& m_run, Stats& st, bool real) {
-    MaxState ms;
+                                                 f32x16 (&nxt)[KB], float c2, float m_use) {
     mfma_pipeline_woven<PV_NI, T::PDEPTH, Op>(
         [&](int i) __attribute__((always_inline)) { return v_read(vbase, i, ln); },
         [&](int i, const Op& a) __attribute__((always_inline)) { T::pv_mma(oacc, i / NDB, i % NDB, a, pf); },
-        [&](auto sl) __attribute__((always_inline)) { max_slice<decltype(sl)::value>(nxt, c2, m_run, st, ms, real); });
+        [&](auto sl) __attribute__((always_inline)) {
+          constexpr int v0 = decltype(sl)::value * X_PER_SLOT;
+#pragma unroll
+          for (int v = v0; v < v0 + X_PER_SLOT; ++v)
+            nxt[v / 16][v % 16] = __builtin_fmaf(nxt[v / 16][v % 16], c2, -m_use);
+        });
     anchor_s(nxt);
   }
 };
@@ -293,8 +247,10 @@ void fa_fwd_pipe_kernel(Params p) {
   {
     T::qk(sa, kslot(0), q, ln);
     if (needs_mask(0)) T::mask(sa, last_key);
-    typename W::Stats st;
-    W::scores_to_exponents(sa, c2, m_run, st);   // O and l are still 0: no rescale
+    // the first base is tile 0's row max (every row sees key 0, so it is
+    // finite); O and l are still 0, so nothing is rescaled
+    m_run = T::row_max(sa) * c2;
+    T::to_exponents(sa, c2, m_run);
   }
   __syncthreads();                                // every wave is done with K_0's slot
 
@@ -314,16 +270,21 @@ void fa_fwd_pipe_kernel(Params p) {
       const bool real = j + 1 < wave_tiles;     // tile j+1 is one of this wave's tiles
       float psum;
       W::stage_a(nxt, k_use, q, ln, cur, pf, psum);
+      // tile j's exponents were taken against the base in use without its
+      // row max; a lane sum above 2^TAU (or a NaN) means some probability
+      // passed 2^TAU: take the row max, move the bases that grew by more than
+      // TAU, redo the tile's probabilities and rescale O and l (before P_j V_j)
+      if (__builtin_amdgcn_ballot_w64(!(psum <= T::TAU_P))) {
+        asm volatile("" ::: "memory");   // a real (rarely taken) branch, not a select
+        const float alpha = T::rebase(cur, m_run);
+        W::probs(cur, pf, psum);
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < NDB; ++b) oacc[b] *= alpha;
+      }
       l_run += psum;
       if (real && needs_mask(j + 1)) T::mask(nxt, last_key - (j + 1) * BC);
-      typename W::Stats st;
-      W::stage_b(oacc, v_use, pf, ln, nxt, c2, m_run, st, real);
-      if (__builtin_amdgcn_ballot_w64(st.grow)) {
-        asm volatile("" ::: "memory");   // a real (rarely taken) branch, not a select
-        l_run *= st.alpha;
-#pragma unroll
-        for (int b = 0; b < NDB; ++b) oacc[b] *= st.alpha;
-      }
+      W::stage_b(oacc, v_use, pf, ln, nxt, c2, m_run);
     }
     wait_vmcnt<0>();      // K_{j+2} and V_{j+1} have landed
     __syncthreads();

@@ -37,6 +37,7 @@ struct Tile {
   // O / l) and L subtracts it back.
   static constexpr float TAU = MODE == MODE_FP8 ? 2.f : 8.f;
   static constexpr float EXP_SHIFT = MODE == MODE_FP8 ? 8.f - TAU : 0.f;
+  static constexpr float TAU_P = MODE == MODE_FP8 ? 4.f : 256.f;   // 2^TAU
 
   // the wave's 32 queries as the B operand of S^T = K Q^T
   struct QFrag {
@@ -365,6 +366,74 @@ struct Tile {
       softmax_slice<A>(st, sm, m_run, c2, pf);
       softmax_slices<A + 1, B>(st, sm, m_run, c2, pf);
     }
+  }
+
+  // ---- the online-softmax step with the row max taken only when needed
+  // (bf16).  Once every row of the wave has a finite running max, a tile's
+  // exponentials are taken against the base already in use, without the
+  // tile's row max.  Every P is >= 0, so a lane sum of at most 2^TAU bounds
+  // each of the lane's probabilities by 2^TAU: the base could stay, which is
+  // what the lazy rule decides from the max.  A larger sum (or a NaN) sends
+  // the wave through the exact order: the row max of the exponents, the new
+  // base where a row grew by more than TAU, the tile's exponentials again,
+  // and O and l rescaled.  Bases, probabilities and rescales are those of
+  // the max-first order; what is saved is the max of every other tile.
+  static constexpr bool SPEC = MODE == MODE_BF16;
+
+  // the row max of st over both lane halves
+  static __device__ __forceinline__ float row_max(const f32x16 (&st)[KB]) {
+    float m[2 * KB];
+#pragma unroll
+    for (int h = 0; h < 2 * KB; ++h) {
+      const int kb = h / 2, i0 = 8 * (h % 2);
+      m[h] = st[kb][i0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m[h] = __builtin_elementwise_maximum(m[h], st[kb][i0 + i]);
+    }
+#pragma unroll
+    for (int h = 1; h < 2 * KB; ++h) m[0] = __builtin_elementwise_maximum(m[0], m[h]);
+    return swap_halves_max(m[0]);
+  }
+  // st <- c2 * st - m_use (scores to exponents, log2 units)
+  static __device__ __forceinline__ void to_exponents(f32x16 (&st)[KB], float c2, float m_use) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[kb][i] = __builtin_fmaf(st[kb][i], c2, -m_use);
+  }
+  // P = 2^x packed as the P.V operand (x is kept); returns this lane's sum
+  // of the fp32 probabilities
+  static __device__ __forceinline__ float probs(const f32x16 (&x)[KB], PFrag& pf) {
+    static_assert(MODE == MODE_BF16, "bf16 P operand");
+    float sum[2];
+#pragma unroll
+    for (int g = 0; g < 4 * KB; ++g) {
+      const int kb = g / 4, i0 = 4 * (g % 4);
+      const float e0 = __builtin_amdgcn_exp2f(x[kb][i0]), e1 = __builtin_amdgcn_exp2f(x[kb][i0 + 1]);
+      const float e2 = __builtin_amdgcn_exp2f(x[kb][i0 + 2]), e3 = __builtin_amdgcn_exp2f(x[kb][i0 + 3]);
+      // step g/2, words 2*(g%2) and 2*(g%2)+1 <- scores 4g .. 4g+3 of the tile
+      pf.h[g / 2][2 * (g % 2)] = (int)pack_bf16x2(e0, e1);
+      pf.h[g / 2][2 * (g % 2) + 1] = (int)pack_bf16x2(e2, e3);
+      const float part = (e0 + e1) + (e2 + e3);
+      sum[g & 1] = g < 2 ? part : sum[g & 1] + part;
+    }
+    return sum[0] + sum[1];
+  }
+  // the max-first order for a tile whose exponents x were taken against
+  // the base in use (0 for a row without one) and let some probability pass
+  // 2^TAU: a row whose max grew by more than TAU (a row without a base: that
+  // saw any key) moves its base to that max and its exponents with it.
+  // Returns alpha = 2^(m_old - m_new) for O and l (1: base kept or new).
+  static __device__ __forceinline__ float rebase(f32x16 (&x)[KB], float& m_run) {
+    const float mx = row_max(x);
+    const bool fresh = m_run == -INFINITY;
+    const bool grow = fresh ? mx > -INFINITY : mx > TAU;
+    const float delta = grow ? mx : 0.f;
+    m_run = fresh ? (grow ? mx : m_run) : m_run + delta;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) x[kb] -= delta;
+    // (a row without a base has O = 0 and l = 0: its factor stays 1)
+    return grow && !fresh ? __builtin_amdgcn_exp2f(-delta) : 1.f;
   }
 
   // oacc += V^T P^T for the tile at vbase
