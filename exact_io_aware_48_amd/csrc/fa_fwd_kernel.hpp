@@ -71,9 +71,24 @@ namespace fa {
 // blocks, so that a wave leaving its matrix work gets its softmax through
 // ahead of the other wave's MFMA issue (measured at d = 256: +1% to +6%
 // depending on the GPU session; none or a loss at d = 64 and 128).
-template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false, int VAR = VAR_NONE, bool PRIO = false>
+// RP > 0: each step, a wave takes an issue priority that grows with the key
+// tiles its workgroup still has to stream (above 4 RP: 3, 2 RP: 2, RP: 1,
+// else 0).  Workgroups sharing a CU then advance together, and the one with
+// the most work left goes first, instead of the oldest waves finishing early
+// and leaving the last workgroup alone on the CU.
+template <int RP>
+__device__ __forceinline__ void prio_by_remaining(int rem) {
+  if (rem > 4 * RP) __builtin_amdgcn_s_setprio(3);
+  else if (rem > 2 * RP) __builtin_amdgcn_s_setprio(2);
+  else if (rem > RP) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false, int VAR = VAR_NONE, bool PRIO = false,
+          int RP = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(Params p) {
+  static_assert(!(PRIO && RP), "one priority scheme");
   static_assert(VAR == VAR_NONE || !PP, "variants: no ping-pong");
   static_assert(VAR != VAR_BLOCKSPARSE || ((32 * NW) % kMaskBlock == 0 && kMaskBlock % BC == 0),
                 "row blocks and key tiles nest in the mask blocks");
@@ -311,6 +326,7 @@ void fa_fwd_kernel(Params p) {
       // two-slot ring: step j uses slot j % 2 and fills the other; unrolled
       // by two so that the slot offsets are constants of the LDS instructions
       auto step = [&](int j, int sl) __attribute__((always_inline)) {
+        if constexpr (RP > 0) prio_by_remaining<RP>(n_tiles - j);
         const bool more = j + 1 < n_tiles;
         if (more) {                     // start fetching tile j+1 into the free slots
           if constexpr (DMA) issue_tile(j + 1, kslot(sl ^ 1), vslot(sl ^ 1));

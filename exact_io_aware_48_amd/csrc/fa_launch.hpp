@@ -36,9 +36,10 @@ struct Tile {
 // PIPE: the software-pipelined kernel (fa_pipe_kernel.hpp), whose waves weave
 // each tile's softmax into the neighbouring tiles' MFMAs (bf16, d = 128).
 template <int MODE, int D> struct Cfg;
-template <int BC_, int NW_, bool PP_, bool PRIO_ = false, bool PIPE_ = false> struct Shape {
+template <int BC_, int NW_, bool PP_, bool PRIO_ = false, bool PIPE_ = false, int RP_ = 0> struct Shape {
   static constexpr int BC = BC_, NW = NW_;
   static constexpr bool PP = PP_, PRIO = PRIO_, PIPE = PIPE_;
+  static constexpr int RP = RP_;
 };
 template <> struct Cfg<fa::MODE_BF16, 64> : Shape<64, 4, false> {};
 template <> struct Cfg<fa::MODE_BF16, 128> : Shape<64, 8, false, false, true> {};
@@ -59,7 +60,8 @@ template <> struct VarCfg<fa::MODE_BF16, 128> : Shape<128, 8, false> {};
 template <int MODE, int D>
 Tile tile_for() {
   using C = Cfg<MODE, D>;
-  return Tile{C::BC, C::NW, fa::Geo<D, C::BC, C::NW, MODE, C::PP>::LDSB};
+  // the pipelined kernel also stages its Q tile in LDS
+  return Tile{C::BC, C::NW, fa::Geo<D, C::BC, C::NW, MODE, C::PP>::LDSB + (C::PIPE ? 32 * C::NW * D * 2 : 0)};
 }
 
 Tile lookup_tile(int mode, int d) {
@@ -85,7 +87,8 @@ hipError_t launch(const Params& p, int grid, hipStream_t stream) {
   if constexpr (VAR == fa::VAR_NONE && C::PIPE)
     kern = &fa::fa_fwd_pipe_kernel<D, BC, NW, CAUSAL>;
   else
-    kern = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR, VAR == fa::VAR_NONE && C::PRIO>;
+    kern = &fa::fa_fwd_kernel<D, BC, NW, MODE, CAUSAL, C::PP, VAR, VAR == fa::VAR_NONE && C::PRIO,
+                              VAR == fa::VAR_NONE ? C::RP : 0>;
   Params args = p;
   if constexpr (CAUSAL) {
     static std::atomic<int> cache[kMaxDevices];   // one per kernel

@@ -190,7 +190,9 @@ void fa_fwd_pipe_kernel(Params p) {
   constexpr int KB = W::KB, NDB = W::NDB;
   static_assert(G::KST == 2 && G::VST == 2, "two-slot K and V rings");
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[G::LDSB];
+  // K and V rings, then the Q tile (prologue); the O tile reuses the rings
+  constexpr int QTILEB = G::BR * T::QROWB;
+  __shared__ __attribute__((aligned(16))) char smem_raw[G::LDSB + QTILEB];
   char FA_LDS* const smem = (char FA_LDS*)(smem_raw);
   auto kslot = [&](int s) __attribute__((always_inline)) { return smem + s * G::SLOTB; };
   auto vslot = [&](int s) __attribute__((always_inline)) { return smem + (G::KST + s) * G::SLOTB; };
@@ -213,8 +215,9 @@ void fa_fwd_pipe_kernel(Params p) {
   const int n_tiles = CAUSAL ? min(tiles_all, (q_row0 + G::BR - 1) / BC + 1) : tiles_all;
   const int wave_tiles = CAUSAL ? min(tiles_all, (qw0 + 31) / BC + 1) : tiles_all;
 
-  typename T::QFrag q;
-  T::load_q(p, head_off, my_q, ln, q);
+  // the Q tile goes to LDS with the first K/V tiles (whole rows per DMA)
+  char FA_LDS* const qtile = smem + G::LDSB;
+  T::dma_q(static_cast<const char*>(p.q) + head_off * 2 + (int64_t)q_row0 * T::QROWB, N - q_row0, qtile, wave, lane);
 
   Stager<D, BC, NW, MODE_BF16, false> kstage;
   Stager<D, BC, NW, MODE_BF16, true> vstage;
@@ -244,6 +247,8 @@ void fa_fwd_pipe_kernel(Params p) {
   if (1 < n_tiles) kstage.issue(kglob, 1, N, kslot(1), wave, lane);
   wait_vmcnt<0>();
   __syncthreads();
+  typename T::QFrag q;
+  T::load_q_lds(qtile, wave, ln, p.qsign, q);
   {
     T::qk(sa, kslot(0), q, ln);
     if (needs_mask(0)) T::mask(sa, last_key);
@@ -296,7 +301,8 @@ void fa_fwd_pipe_kernel(Params p) {
   }
   if (j < n_tiles) step(j, sa, sb, 0);
 
-  T::store(p, head_off, bh, my_q, ln, oacc, m_run, l_run);
+  // the last step ended with a barrier: the rings are free for the O tile
+  T::store_lds(p, head_off, bh, qw0, my_q, ln, oacc, m_run, l_run, smem + wave * 32 * T::QROWB, lane);
 }
 
 }  // namespace fa

@@ -153,6 +153,79 @@ struct Tile {
     }
   }
 
+  // ---- Q and O through LDS (bf16).  A wave's direct loads of its Q slice
+  // touch 32 rows of 16 bytes per instruction, and so do the stores of O^T
+  // from the accumulator layout.  Staged through LDS, every HBM access is a
+  // run of whole rows (1 KiB per wave instruction); the LDS tile uses the K
+  // swizzle (16-byte chunk c of row r at chunk c ^ swz_k(r)).
+  static constexpr int QROWB = D * 2;                 // bytes per bf16 row
+  static constexpr int QCPR = QROWB / 16;
+
+  // the workgroup's BR = 32 NW rows starting at gsrc (rows_valid of them
+  // exist; later ones re-read the last, whose scores stay in their own
+  // rows, which are never stored) -> LDS at dst, one DMA per 1 KiB
+  static __device__ __forceinline__ void dma_q(const char* gsrc, int rows_valid, char FA_LDS* dst, int wave, int lane) {
+    static_assert(MODE == MODE_BF16, "bf16 rows");
+    constexpr int PER = 32 * NW * QCPR / (NW * 64);   // chunks per thread
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = (i * NW + wave) * 64 + lane;
+      const int r = u / QCPR, pc = u % QCPR;
+      const int off = min(r, rows_valid - 1) * QROWB + ((pc ^ swz_k<QCPR>(r)) << 4);
+      dma16_s(gsrc, off, dst + (i * NW + wave) * 1024);
+    }
+  }
+  // this wave's Q slice from the staged tile (qsign flips the sign bits
+  // when the softmax scale is negative)
+  static __device__ __forceinline__ void load_q_lds(const char FA_LDS* qtile, int wave, const Lane& ln, uint32_t qsign,
+                                                    QFrag& q) {
+    static_assert(MODE == MODE_BF16 && PIPE_ADDR && QROWB == G::ROWB, "K-tile addressing");
+    const int sgn = (int)qsign;
+    const char FA_LDS* base = qtile + wave * 32 * QROWB;
+#pragma unroll
+    for (int c = 0; c < QK_STEPS; ++c) {
+      i32x4 w = lds_read16(base + ln.ka[c & 7] + ((c >> 3) << 8));
+      w ^= i32x4{sgn, sgn, sgn, sgn};
+      q.a[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  // O = out_mul * O / l for the wave's 32 queries through the wave's own
+  // 32-row LDS region (no other wave touches it), then whole rows to HBM;
+  // L = ln2 * (m + log2 l) as in store()
+  static __device__ __forceinline__ void store_lds(const Params& p, int64_t head_off, int bh, int qw0, int my_q,
+                                                   const Lane& ln, const f32x16 (&oacc)[NDB], float m_run, float l_run,
+                                                   char FA_LDS* region, int lane) {
+    static_assert(MODE == MODE_BF16, "bf16 output");
+    const float l_tot = swap_halves_sum(l_run);
+    const bool seen = l_tot > 0.f;
+    const float inv = seen ? p.out_mul / l_tot : 0.f;
+    if (my_q < p.N && ln.hf == 0)
+      p.lse[(int64_t)bh * p.N + my_q] = seen ? (m_run - EXP_SHIFT + __log2f(l_tot)) * kLn2 : -INFINITY;
+    // lane (n, hf): dims 32 db + 8 g + 4 hf .. + 3 of row n = 8 bytes in chunk 4 db + g
+    char FA_LDS* const rowp = region + ln.n * QROWB;
+    const int sw = swz_k<QCPR>(ln.n);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
+        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        *reinterpret_cast<i32x2 FA_LDS*>(rowp + (((4 * db + g) ^ sw) << 4) + 8 * ln.hf) =
+            i32x2{(int)pack_bf16x2(x0, x1), (int)pack_bf16x2(x2, x3)};
+      }
+    // the reads below fetch other lanes' writes: wait for them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int RPI = 64 / QCPR;   // rows per wave instruction
+    const int rr = lane / QCPR, lc = lane % QCPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + rr;
+      const i32x4 v = lds_read16(region + r * QROWB + ((lc ^ swz_k<QCPR>(r)) << 4));
+      if (qw0 + r < p.N)
+        *reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.o) + head_off + (int64_t)(qw0 + r) * D + 8 * lc) = v;
+    }
+  }
+
   // ---- single MFMA items.  A QK item (c, kb) adds d-step c of key block kb
   // to S^T; a PV item (s, db) adds key-step s to d-block db of O^T.  Each
   // item's A operand is one LDS read (fp8: two, or four transposed reads).
