@@ -382,7 +382,16 @@ void fa_fwd_kernel(Params p) {
     }
   }
 
-  T::store(p, head_off, bh, my_q, ln, oacc, m_run, l_run);
+  if constexpr (MODE == MODE_BF16) {
+    // every loop above ends with a barrier: the rings are free for O, whose
+    // rows leave in whole segments (as many d-blocks per pass as a wave's
+    // share of the rings holds)
+    constexpr int GDB0 = G::LDSB / (NW * 2048);
+    constexpr int GDB = GDB0 >= NDB ? NDB : GDB0;
+    T::template store_lds<GDB>(p, head_off, bh, qw0, my_q, ln, oacc, m_run, l_run, smem + wave * 32 * 64 * GDB, lane);
+  } else {
+    T::store(p, head_off, bh, my_q, ln, oacc, m_run, l_run);
+  }
 }
 
 }  // namespace fa

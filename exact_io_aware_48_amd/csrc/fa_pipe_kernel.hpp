@@ -302,7 +302,7 @@ void fa_fwd_pipe_kernel(Params p) {
   if (j < n_tiles) step(j, sa, sb, 0);
 
   // the last step ended with a barrier: the rings are free for the O tile
-  T::store_lds(p, head_off, bh, qw0, my_q, ln, oacc, m_run, l_run, smem + wave * 32 * T::QROWB, lane);
+  T::template store_lds<NDB>(p, head_off, bh, qw0, my_q, ln, oacc, m_run, l_run, smem + wave * 32 * T::QROWB, lane);
 }
 
 }  // namespace fa

@@ -190,39 +190,50 @@ struct Tile {
     }
   }
   // O = out_mul * O / l for the wave's 32 queries through the wave's own
-  // 32-row LDS region (no other wave touches it), then whole rows to HBM;
-  // L = ln2 * (m + log2 l) as in store()
+  // LDS region (no other wave touches it), then whole row segments to HBM;
+  // L = ln2 * (m + log2 l) as in store().  GDB d-blocks (64 bytes of each
+  // row) per pass: the region holds 32 rows of 64 GDB bytes.
+  template <int GDB>
   static __device__ __forceinline__ void store_lds(const Params& p, int64_t head_off, int bh, int qw0, int my_q,
                                                    const Lane& ln, const f32x16 (&oacc)[NDB], float m_run, float l_run,
                                                    char FA_LDS* region, int lane) {
-    static_assert(MODE == MODE_BF16, "bf16 output");
+    static_assert(MODE == MODE_BF16 && NDB % GDB == 0, "bf16 output in whole passes");
+    constexpr int RB = 64 * GDB, CPRR = RB / 16;    // region row bytes, 16-byte chunks per region row
+    constexpr int RPI = 1024 / RB;                  // rows per wave instruction
     const float l_tot = swap_halves_sum(l_run);
     const bool seen = l_tot > 0.f;
     const float inv = seen ? p.out_mul / l_tot : 0.f;
     if (my_q < p.N && ln.hf == 0)
       p.lse[(int64_t)bh * p.N + my_q] = seen ? (m_run - EXP_SHIFT + __log2f(l_tot)) * kLn2 : -INFINITY;
-    // lane (n, hf): dims 32 db + 8 g + 4 hf .. + 3 of row n = 8 bytes in chunk 4 db + g
-    char FA_LDS* const rowp = region + ln.n * QROWB;
-    const int sw = swz_k<QCPR>(ln.n);
+    char FA_LDS* const rowp = region + ln.n * RB;
+    const int sw = swz_k<CPRR>(ln.n);
+    const int rr = lane / CPRR, lc = lane % CPRR;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int pass = 0; pass < NDB / GDB; ++pass) {
+      // lane (n, hf): dims 32 db + 8 g + 4 hf .. + 3 of row n = 8 bytes of chunk 4 (db - GDB pass) + g
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
-        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
-        *reinterpret_cast<i32x2 FA_LDS*>(rowp + (((4 * db + g) ^ sw) << 4) + 8 * ln.hf) =
-            i32x2{(int)pack_bf16x2(x0, x1), (int)pack_bf16x2(x2, x3)};
+      for (int b = 0; b < GDB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int db = GDB * pass + b;
+          const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
+          const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+          *reinterpret_cast<i32x2 FA_LDS*>(rowp + (((4 * b + g) ^ sw) << 4) + 8 * ln.hf) =
+              i32x2{(int)pack_bf16x2(x0, x1), (int)pack_bf16x2(x2, x3)};
+        }
+      // the reads below fetch other lanes' writes: wait for them (the next
+      // pass's writes come after this pass's reads have returned: their data
+      // feeds the stores)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int r = i * RPI + rr;
+        const i32x4 v = lds_read16(region + r * RB + ((lc ^ swz_k<CPRR>(r)) << 4));
+        if (qw0 + r < p.N)
+          *reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.o) + head_off + (int64_t)(qw0 + r) * D + 32 * GDB * pass +
+                                    8 * lc) = v;
       }
-    // the reads below fetch other lanes' writes: wait for them
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    constexpr int RPI = 64 / QCPR;   // rows per wave instruction
-    const int rr = lane / QCPR, lc = lane % QCPR;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = i * RPI + rr;
-      const i32x4 v = lds_read16(region + r * QROWB + ((lc ^ swz_k<QCPR>(r)) << 4));
-      if (qw0 + r < p.N)
-        *reinterpret_cast<i32x4*>(static_cast<uint16_t*>(p.o) + head_off + (int64_t)(qw0 + r) * D + 8 * lc) = v;
+      asm volatile("" ::: "memory");
     }
   }
 
