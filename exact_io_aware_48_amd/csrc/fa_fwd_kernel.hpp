@@ -124,8 +124,27 @@ void fa_fwd_kernel(Params p) {
   const int n_tiles = CAUSAL ? min(tiles_all, (q_row0 + G::BR - 1) / BC + 1) : tiles_all;
   const int wave_tiles = CAUSAL ? min(tiles_all, (qw0 + 31) / BC + 1) : tiles_all;
 
+  // QSTAGE (bf16, when the Q tile fits the second K and V ring slots, which
+  // the first tile leaves free): Q comes through LDS in whole rows with tile
+  // 0, rows 0 .. BR/2 - 1 in K slot 1 and the rest in V slot 1.  Otherwise
+  // each wave loads its slice directly.
+  constexpr bool QSTAGE = MODE == MODE_BF16 && !PP && 16 * NW <= BC;
   typename T::QFrag q;
-  T::load_q(p, head_off, my_q, ln, q);
+  if constexpr (!QSTAGE) T::load_q(p, head_off, my_q, ln, q);
+  auto stage_q = [&]() __attribute__((always_inline)) {
+    if constexpr (QSTAGE)
+      T::template dma_q<NW * 32 * T::QROWB / 2048>(static_cast<const char*>(p.q) + head_off * 2 + (int64_t)q_row0 * T::QROWB,
+                                                   N - q_row0, kslot(1), vslot(1), wave, lane);
+  };
+  // after the barrier that publishes tile 0 (and Q); a second barrier frees
+  // the slots for tile 1
+  auto take_q = [&]() __attribute__((always_inline)) {
+    if constexpr (QSTAGE) {
+      const char FA_LDS* rows = wave < NW / 2 ? kslot(1) + wave * 32 * T::QROWB : vslot(1) + (wave - NW / 2) * 32 * T::QROWB;
+      T::load_q_lds(rows, ln, p.qsign, q);
+      __syncthreads();
+    }
+  };
 
   // ---------------- K/V tile staging
   // bf16/fp8: direct HBM -> LDS loads.  fp32: HBM -> registers -> hi/lo
@@ -278,16 +297,18 @@ void fa_fwd_kernel(Params p) {
       return j;
     };
     int j = next_needed(0);
+    stage_q();
     if (j < n_tiles) {
       if constexpr (DMA) {
         issue_tile(j, kslot(0), vslot(0));
-        wait_vmcnt<0>();
       } else {
         load_tile(j);
         store_tile(kslot(0), vslot(0));
       }
     }
+    if constexpr (DMA) wait_vmcnt<0>();
     __syncthreads();
+    take_q();
     int cur = 0;
     while (j < n_tiles) {
       const int jn = next_needed(j + 1);
@@ -313,6 +334,7 @@ void fa_fwd_kernel(Params p) {
     // while tile j is used.  The slots refilled in step j held K_{j-1} and
     // V_{j-1} (V_{j-2} with ping-pong), whose last readers finished before the
     // barrier that ended step j-1.
+    stage_q();
     if constexpr (DMA) {
       issue_tile(0, kslot(0), vslot(0));
       wait_vmcnt<0>();
@@ -321,6 +343,7 @@ void fa_fwd_kernel(Params p) {
       store_tile(kslot(0), vslot(0));
     }
     __syncthreads();
+    take_q();
 
     if constexpr (!PP) {
       // two-slot ring: step j uses slot j % 2 and fills the other; unrolled
@@ -382,7 +405,8 @@ void fa_fwd_kernel(Params p) {
     }
   }
 
-  if constexpr (MODE == MODE_BF16) {
+  if constexpr (MODE == MODE_BF16 && !(VAR == VAR_BLOCKSPARSE && D == 256)) {
+    // (not the block-sparse d = 256 instance, where it costs spills)
     // every loop above ends with a barrier: the rings are free for O, whose
     // rows leave in whole segments (as many d-blocks per pass as a wave's
     // share of the rings holds)

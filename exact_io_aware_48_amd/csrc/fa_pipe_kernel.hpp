@@ -217,7 +217,8 @@ void fa_fwd_pipe_kernel(Params p) {
 
   // the Q tile goes to LDS with the first K/V tiles (whole rows per DMA)
   char FA_LDS* const qtile = smem + G::LDSB;
-  T::dma_q(static_cast<const char*>(p.q) + head_off * 2 + (int64_t)q_row0 * T::QROWB, N - q_row0, qtile, wave, lane);
+  T::template dma_q<1 << 30>(static_cast<const char*>(p.q) + head_off * 2 + (int64_t)q_row0 * T::QROWB, N - q_row0, qtile,
+                             qtile, wave, lane);
 
   Stager<D, BC, NW, MODE_BF16, false> kstage;
   Stager<D, BC, NW, MODE_BF16, true> vstage;
@@ -248,7 +249,7 @@ void fa_fwd_pipe_kernel(Params p) {
   wait_vmcnt<0>();
   __syncthreads();
   typename T::QFrag q;
-  T::load_q_lds(qtile, wave, ln, p.qsign, q);
+  T::load_q_lds(qtile + wave * 32 * T::QROWB, ln, p.qsign, q);
   {
     T::qk(sa, kslot(0), q, ln);
     if (needs_mask(0)) T::mask(sa, last_key);

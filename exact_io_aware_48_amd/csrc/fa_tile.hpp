@@ -163,28 +163,33 @@ struct Tile {
 
   // the workgroup's BR = 32 NW rows starting at gsrc (rows_valid of them
   // exist; later ones re-read the last, whose scores stay in their own
-  // rows, which are never stored) -> LDS at dst, one DMA per 1 KiB
-  static __device__ __forceinline__ void dma_q(const char* gsrc, int rows_valid, char FA_LDS* dst, int wave, int lane) {
+  // rows, which are never stored) -> LDS, one DMA per 1 KiB block: blocks
+  // below SPLIT to dst_a + 1024 b, the others to dst_b + 1024 (b - SPLIT)
+  // (two free ring slots can hold the tile)
+  template <int SPLIT>
+  static __device__ __forceinline__ void dma_q(const char* gsrc, int rows_valid, char FA_LDS* dst_a, char FA_LDS* dst_b,
+                                               int wave, int lane) {
     static_assert(MODE == MODE_BF16, "bf16 rows");
     constexpr int PER = 32 * NW * QCPR / (NW * 64);   // chunks per thread
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int u = (i * NW + wave) * 64 + lane;
+      const int blk = i * NW + wave;
+      const int u = blk * 64 + lane;
       const int r = u / QCPR, pc = u % QCPR;
       const int off = min(r, rows_valid - 1) * QROWB + ((pc ^ swz_k<QCPR>(r)) << 4);
-      dma16_s(gsrc, off, dst + (i * NW + wave) * 1024);
+      dma16_s(gsrc, off, blk < SPLIT ? dst_a + blk * 1024 : dst_b + (blk - SPLIT) * 1024);
     }
   }
-  // this wave's Q slice from the staged tile (qsign flips the sign bits
-  // when the softmax scale is negative)
-  static __device__ __forceinline__ void load_q_lds(const char FA_LDS* qtile, int wave, const Lane& ln, uint32_t qsign,
+  // this wave's Q slice from its 32 staged rows at wave_rows (the row
+  // swizzle repeats every 16 rows) -- qsign flips the sign bits when the
+  // softmax scale is negative
+  static __device__ __forceinline__ void load_q_lds(const char FA_LDS* wave_rows, const Lane& ln, uint32_t qsign,
                                                     QFrag& q) {
     static_assert(MODE == MODE_BF16 && PIPE_ADDR && QROWB == G::ROWB, "K-tile addressing");
     const int sgn = (int)qsign;
-    const char FA_LDS* base = qtile + wave * 32 * QROWB;
 #pragma unroll
     for (int c = 0; c < QK_STEPS; ++c) {
-      i32x4 w = lds_read16(base + ln.ka[c & 7] + ((c >> 3) << 8));
+      i32x4 w = lds_read16(wave_rows + ln.ka[c & 7] + ((c >> 3) << 8));
       w ^= i32x4{sgn, sgn, sgn, sgn};
       q.a[c] = __builtin_bit_cast(bf16x8, w);
     }
