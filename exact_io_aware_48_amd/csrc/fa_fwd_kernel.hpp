@@ -84,6 +84,25 @@ __device__ __forceinline__ void prio_by_remaining(int rem) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
+// How the kernel brings in its Q tile (bf16 and fp8): 1 = through the second
+// K and V ring slots, which tile 0 leaves free (the tile fits them: rows
+// 0 .. BR/2 - 1 in K slot 1, the rest in V slot 1); 2 = through an LDS region
+// of its own (eight-wave workgroups, which run one per CU at their register
+// counts, when it fits the LDS); 0 = each wave loads its slice directly.
+template <int D, int BC, int NW, int MODE, bool PP>
+constexpr int q_stage_mode() {
+  if (MODE == MODE_F32 || PP) return 0;
+  using G = Geo<D, BC, NW, MODE, PP>;
+  constexpr int qtile = 32 * NW * D * (MODE == MODE_FP8 ? 1 : 2);
+  if (qtile <= 2 * G::SLOTB) return 1;
+  if (NW == 8 && G::LDSB + qtile <= 160 * 1024) return 2;
+  return 0;
+}
+template <int D, int BC, int NW, int MODE, bool PP>
+constexpr int q_region_bytes() {
+  return q_stage_mode<D, BC, NW, MODE, PP>() == 2 ? 32 * NW * D * (MODE == MODE_FP8 ? 1 : 2) : 0;
+}
+
 template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false, int VAR = VAR_NONE, bool PRIO = false,
           int RP = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -97,7 +116,10 @@ void fa_fwd_kernel(Params p) {
   constexpr int NDB = T::NDB;
   constexpr bool DMA = MODE != MODE_F32;
 
-  __shared__ __attribute__((aligned(16))) char smem_raw[G::LDSB];
+  // (the ALiBi fp8 instances keep direct Q loads: a region costs them spills)
+  constexpr int QMODE0 = q_stage_mode<D, BC, NW, MODE, PP>();
+  constexpr int QMODE = QMODE0 == 2 && VAR == VAR_ALIBI && MODE == MODE_FP8 ? 0 : QMODE0;
+  __shared__ __attribute__((aligned(16))) char smem_raw[G::LDSB + (QMODE == 2 ? q_region_bytes<D, BC, NW, MODE, PP>() : 0)];
   char FA_LDS* const smem = (char FA_LDS*)(smem_raw);  // generic -> LDS address space
   // K ring slots first, then V ring slots
   auto kslot = [&](int s) __attribute__((always_inline)) { return smem + s * G::SLOTB; };
@@ -124,25 +146,26 @@ void fa_fwd_kernel(Params p) {
   const int n_tiles = CAUSAL ? min(tiles_all, (q_row0 + G::BR - 1) / BC + 1) : tiles_all;
   const int wave_tiles = CAUSAL ? min(tiles_all, (qw0 + 31) / BC + 1) : tiles_all;
 
-  // QSTAGE (bf16, when the Q tile fits the second K and V ring slots, which
-  // the first tile leaves free): Q comes through LDS in whole rows with tile
-  // 0, rows 0 .. BR/2 - 1 in K slot 1 and the rest in V slot 1.  Otherwise
-  // each wave loads its slice directly.
-  constexpr bool QSTAGE = MODE == MODE_BF16 && !PP && 16 * NW <= BC;
+  // Q through LDS in whole rows with tile 0 (q_stage_mode), or each wave's
+  // slice directly
   typename T::QFrag q;
-  if constexpr (!QSTAGE) T::load_q(p, head_off, my_q, ln, q);
+  if constexpr (QMODE == 0) T::load_q(p, head_off, my_q, ln, q);
+  const char* const qglob = static_cast<const char*>(p.q) + head_off * T::QROWB / D + (int64_t)q_row0 * T::QROWB;
   auto stage_q = [&]() __attribute__((always_inline)) {
-    if constexpr (QSTAGE)
-      T::template dma_q<NW * 32 * T::QROWB / 2048>(static_cast<const char*>(p.q) + head_off * 2 + (int64_t)q_row0 * T::QROWB,
-                                                   N - q_row0, kslot(1), vslot(1), wave, lane);
+    if constexpr (QMODE == 1)
+      T::template dma_q<NW * 32 * T::QROWB / 2048>(qglob, N - q_row0, kslot(1), vslot(1), wave, lane);
+    else if constexpr (QMODE == 2)
+      T::template dma_q<1 << 30>(qglob, N - q_row0, smem + G::LDSB, smem + G::LDSB, wave, lane);
   };
-  // after the barrier that publishes tile 0 (and Q); a second barrier frees
-  // the slots for tile 1
+  // after the barrier that publishes tile 0 (and Q); in the ring slots, a
+  // second barrier frees them for tile 1
   auto take_q = [&]() __attribute__((always_inline)) {
-    if constexpr (QSTAGE) {
+    if constexpr (QMODE == 1) {
       const char FA_LDS* rows = wave < NW / 2 ? kslot(1) + wave * 32 * T::QROWB : vslot(1) + (wave - NW / 2) * 32 * T::QROWB;
       T::load_q_lds(rows, ln, p.qsign, q);
       __syncthreads();
+    } else if constexpr (QMODE == 2) {
+      T::load_q_lds(smem + G::LDSB + wave * 32 * T::QROWB, ln, p.qsign, q);
     }
   };
 
@@ -405,8 +428,11 @@ void fa_fwd_kernel(Params p) {
     }
   }
 
-  if constexpr (MODE == MODE_BF16 && !(VAR == VAR_BLOCKSPARSE && D == 256)) {
-    // (not the block-sparse d = 256 instance, where it costs spills)
+  // (not at d = 256 for the block-sparse bf16 instances and the causal or
+  // variant fp8 ones, where it costs spills)
+  constexpr bool O_STAGE = MODE != MODE_F32 && !(D == 256 && ((MODE == MODE_BF16 && VAR == VAR_BLOCKSPARSE) ||
+                                                              (MODE == MODE_FP8 && (CAUSAL || VAR != VAR_NONE))));
+  if constexpr (O_STAGE) {
     // every loop above ends with a barrier: the rings are free for O, whose
     // rows leave in whole segments (as many d-blocks per pass as a wave's
     // share of the rings holds)

@@ -153,12 +153,13 @@ struct Tile {
     }
   }
 
-  // ---- Q and O through LDS (bf16).  A wave's direct loads of its Q slice
-  // touch 32 rows of 16 bytes per instruction, and so do the stores of O^T
-  // from the accumulator layout.  Staged through LDS, every HBM access is a
-  // run of whole rows (1 KiB per wave instruction); the LDS tile uses the K
-  // swizzle (16-byte chunk c of row r at chunk c ^ swz_k(r)).
-  static constexpr int QROWB = D * 2;                 // bytes per bf16 row
+  // ---- Q and O through LDS (bf16 and fp8 inputs, bf16 output).  A wave's
+  // direct loads of its Q slice touch 32 rows of 16 or 32 bytes per
+  // instruction, and so do the stores of O^T from the accumulator layout.
+  // Staged through LDS, every HBM access is a run of whole rows (1 KiB per
+  // wave instruction); the LDS tile uses the K swizzle (16-byte chunk c of
+  // row r at chunk c ^ swz_k(r)).
+  static constexpr int QROWB = D * (MODE == MODE_FP8 ? 1 : 2);   // bytes per Q row
   static constexpr int QCPR = QROWB / 16;
 
   // the workgroup's BR = 32 NW rows starting at gsrc (rows_valid of them
@@ -169,7 +170,7 @@ struct Tile {
   template <int SPLIT>
   static __device__ __forceinline__ void dma_q(const char* gsrc, int rows_valid, char FA_LDS* dst_a, char FA_LDS* dst_b,
                                                int wave, int lane) {
-    static_assert(MODE == MODE_BF16, "bf16 rows");
+    static_assert(MODE != MODE_F32, "16-bit or 8-bit rows");
     constexpr int PER = 32 * NW * QCPR / (NW * 64);   // chunks per thread
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -185,13 +186,27 @@ struct Tile {
   // softmax scale is negative
   static __device__ __forceinline__ void load_q_lds(const char FA_LDS* wave_rows, const Lane& ln, uint32_t qsign,
                                                     QFrag& q) {
-    static_assert(MODE == MODE_BF16 && PIPE_ADDR && QROWB == G::ROWB, "K-tile addressing");
+    static_assert(MODE != MODE_F32 && QROWB == G::ROWB, "K-tile addressing");
     const int sgn = (int)qsign;
+    if constexpr (MODE == MODE_BF16) {
 #pragma unroll
-    for (int c = 0; c < QK_STEPS; ++c) {
-      i32x4 w = lds_read16(wave_rows + ln.ka[c & 7] + ((c >> 3) << 8));
-      w ^= i32x4{sgn, sgn, sgn, sgn};
-      q.a[c] = __builtin_bit_cast(bf16x8, w);
+      for (int c = 0; c < QK_STEPS; ++c) {
+        i32x4 w = lds_read16(wave_rows + ln.ka[c & 7] + ((c >> 3) << 8));
+        w ^= i32x4{sgn, sgn, sgn, sgn};
+        q.a[c] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+      // step c: chunks 4c + 2 hf and 4c + 2 hf + 1 of row n (as k_operand)
+      const char FA_LDS* rp = wave_rows + ln.n * QROWB;
+      const int sw = swz_k<QCPR>(ln.n);
+#pragma unroll
+      for (int c = 0; c < QK_STEPS; ++c) {
+        i32x4 w0 = lds_read16(rp + (((4 * c + 2 * ln.hf) ^ sw) << 4));
+        i32x4 w1 = lds_read16(rp + (((4 * c + 2 * ln.hf + 1) ^ sw) << 4));
+        w0 ^= i32x4{sgn, sgn, sgn, sgn};
+        w1 ^= i32x4{sgn, sgn, sgn, sgn};
+        q.f8[c] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      }
     }
   }
   // O = out_mul * O / l for the wave's 32 queries through the wave's own
@@ -202,7 +217,7 @@ struct Tile {
   static __device__ __forceinline__ void store_lds(const Params& p, int64_t head_off, int bh, int qw0, int my_q,
                                                    const Lane& ln, const f32x16 (&oacc)[NDB], float m_run, float l_run,
                                                    char FA_LDS* region, int lane) {
-    static_assert(MODE == MODE_BF16 && NDB % GDB == 0, "bf16 output in whole passes");
+    static_assert(MODE != MODE_F32 && NDB % GDB == 0, "bf16 output in whole passes");
     constexpr int RB = 64 * GDB, CPRR = RB / 16;    // region row bytes, 16-byte chunks per region row
     constexpr int RPI = 1024 / RB;                  // rows per wave instruction
     const float l_tot = swap_halves_sum(l_run);
