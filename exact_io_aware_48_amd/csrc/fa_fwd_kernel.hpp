@@ -275,10 +275,10 @@ void fa_fwd_kernel(Params p) {
       bool max_first = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) != 0;
       float alpha = 1.f, psum;
       for (;;) {
-        T::to_exponents(st, c2, m_run == -INFINITY ? 0.f : m_run);
+        T::to_exponents(st, c2, T::m_use(m_run));
         if (max_first) alpha = T::rebase(st, m_run);
         psum = T::probs(st, pf);
-        if (max_first || !__builtin_amdgcn_ballot_w64(!(psum <= T::TAU_P))) break;
+        if (max_first || !__builtin_amdgcn_ballot_w64(!(psum <= T::SPEC_LIMIT))) break;
         asm volatile("" ::: "memory");   // a real (rarely taken) branch
         max_first = true;
         scores(j, kbase, st);
@@ -428,10 +428,9 @@ void fa_fwd_kernel(Params p) {
     }
   }
 
-  // (not at d = 256 for the block-sparse bf16 instances and the causal or
-  // variant fp8 ones, where it costs spills)
-  constexpr bool O_STAGE = MODE != MODE_F32 && !(D == 256 && ((MODE == MODE_BF16 && VAR == VAR_BLOCKSPARSE) ||
-                                                              (MODE == MODE_FP8 && (CAUSAL || VAR != VAR_NONE))));
+  // (not at d = 256 for the block-sparse bf16 instances and the fp8 ones,
+  // where it costs spills)
+  constexpr bool O_STAGE = MODE != MODE_F32 && !(D == 256 && (MODE == MODE_FP8 || VAR == VAR_BLOCKSPARSE));
   if constexpr (O_STAGE) {
     // every loop above ends with a barrier: the rings are free for O, whose
     // rows leave in whole segments (as many d-blocks per pass as a wave's

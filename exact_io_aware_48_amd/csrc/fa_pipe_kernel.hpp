@@ -280,7 +280,7 @@ void fa_fwd_pipe_kernel(Params p) {
       // row max; a lane sum above 2^TAU (or a NaN) means some probability
       // passed 2^TAU: take the row max, move the bases that grew by more than
       // TAU, redo the tile's probabilities and rescale O and l (before P_j V_j)
-      if (__builtin_amdgcn_ballot_w64(!(psum <= T::TAU_P))) {
+      if (__builtin_amdgcn_ballot_w64(!(psum <= T::SPEC_LIMIT))) {
         asm volatile("" ::: "memory");   // a real (rarely taken) branch, not a select
         const float alpha = T::rebase(cur, m_run);
         W::probs(cur, pf, psum);

@@ -37,7 +37,6 @@ struct Tile {
   // O / l) and L subtracts it back.
   static constexpr float TAU = MODE == MODE_FP8 ? 2.f : 8.f;
   static constexpr float EXP_SHIFT = MODE == MODE_FP8 ? 8.f - TAU : 0.f;
-  static constexpr float TAU_P = MODE == MODE_FP8 ? 4.f : 256.f;   // 2^TAU
 
   // the wave's 32 queries as the B operand of S^T = K Q^T
   struct QFrag {
@@ -478,12 +477,21 @@ struct Tile {
   // tile's row max.  Every P is >= 0, so a lane sum of at most 2^TAU bounds
   // each of the lane's probabilities by 2^TAU: the base could stay, which is
   // what the lazy rule decides from the max.  A larger sum (or a NaN) sends
-  // the wave through the exact order: the row max of the exponents, the new
-  // base where a row grew by more than TAU, the tile's exponentials again,
-  // and O and l rescaled.  Bases, probabilities and rescales are those of
-  // the max-first order; what is saved is the max of every other tile.
+  // the wave through the max-first order (rebase): the row max of the
+  // exponents, a new base where a row grew by more than TAU, the tile's
+  // exponentials again, and O and l rescaled.  Bases, probabilities and
+  // rescales are those of the max-first order; what is saved is the max of
+  // every other tile.  (fp8, whose lag of 2 under a 2^6 pre-scale leaves
+  // no such margin, measured slower with a 448 bound and exact rebases:
+  // 1.88 -> 1.91 ms at d = 256, 0.338 -> 0.391 ms long causal d = 128.)
   static constexpr bool SPEC = MODE == MODE_BF16;
+  static constexpr float SPEC_LIMIT = 256.f;   // 2^TAU
+  static constexpr float RTAU = TAU;
 
+  // the exponent base of a row with running max m_run (0 before any key)
+  static __device__ __forceinline__ float m_use(float m_run) {
+    return m_run == -INFINITY ? 0.f : m_run - EXP_SHIFT;
+  }
   // the row max of st over both lane halves
   static __device__ __forceinline__ float row_max(const f32x16 (&st)[KB]) {
     float m[2 * KB];
@@ -524,14 +532,14 @@ struct Tile {
     return sum[0] + sum[1];
   }
   // the max-first order for a tile whose exponents x were taken against
-  // the base in use (0 for a row without one) and let some probability pass
-  // 2^TAU: a row whose max grew by more than TAU (a row without a base: that
-  // saw any key) moves its base to that max and its exponents with it.
-  // Returns alpha = 2^(m_old - m_new) for O and l (1: base kept or new).
+  // the base m_use(m_run) and whose lane sums passed SPEC_LIMIT: a row whose
+  // max passed the base by more than RTAU (a row without a base: that saw
+  // any key) moves its base to that max and its exponents with it.  Returns
+  // alpha = 2^(m_old - m_new) for O and l (1: base kept or new).
   static __device__ __forceinline__ float rebase(f32x16 (&x)[KB], float& m_run) {
     const float mx = row_max(x);
     const bool fresh = m_run == -INFINITY;
-    const bool grow = fresh ? mx > -INFINITY : mx > TAU;
+    const bool grow = fresh ? mx > -INFINITY : mx > RTAU;
     const float delta = grow ? mx : 0.f;
     m_run = fresh ? (grow ? mx : m_run) : m_run + delta;
 #pragma unroll
