@@ -54,6 +54,7 @@ levels from the amdgpu kernel driver's sysfs files right after the headline's ti
                                                write profiles/traffic_<NAME>.json from two PMC runs
     python bench.py --summarize-counters DIR... --workload NAME
                                                write profiles/counters_<NAME>.txt from SQ counter passes
+    python bench.py --timeline NAME...         per-workgroup phase timeline of one launch (diagnostic build)
 """
 
 import argparse
@@ -622,6 +623,76 @@ def roofline_block(w, t):
     return blk
 
 
+# ------------------------------------------------------------------ timeline
+def timeline_summary(w, lib, launches=200):
+    """Per-workgroup phases of one forward launch on workload w, from the
+    diagnostic timeline build (fa_timeline_read): where the time goes between
+    the workgroups' Q/first-tile loads, main loops and O stores, how the work
+    spreads over CUs and XCDs, and how workgroups that share a CU progress.
+    Times in microseconds (100 MHz s_memrealtime stamps)."""
+    import collections
+    import ctypes
+    import numpy as np
+    import torch
+    x, q, k, v = device_inputs(w)
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k, v, o, lse)]
+    code = {"f32": 0, "bf16": 1, "fp8": 2}[w.dtype]
+    if w.dtype == "fp8":
+        call = lambda: lib.fa_fwd_gqa_fp8(*ptrs, w.B, w.H, w.kv_heads, w.N, w.d, w.softmax_scale, *x.descale,
+                                          int(w.causal), s)
+    else:
+        call = lambda: lib.fa_fwd_gqa(*ptrs, w.B, w.H, w.kv_heads, w.N, w.d, w.softmax_scale, int(w.causal), code, s)
+    for _ in range(launches):                 # warm caches and clocks; the last launch is the one read
+        assert call() == 0
+    torch.cuda.synchronize()
+    grid = ctypes.c_int64()
+    i32 = ctypes.c_int
+    assert lib.fa_plan(w.B, w.H, w.N, w.d, int(w.causal), code, ctypes.byref(i32()), ctypes.byref(i32()),
+                       ctypes.byref(grid), ctypes.byref(i32()), ctypes.byref(i32()), ctypes.byref(ctypes.c_int64())) == 0
+    nwg = grid.value
+    buf = np.zeros(nwg * 6, dtype=np.uint64)
+    assert lib.fa_timeline_read(buf.ctypes.data, buf.nbytes) == 0
+    t = buf.reshape(nwg, 6).astype(np.int64)
+    t0 = t[:, 0].min()
+    st, pro, lp, en = ((t[:, i] - t0) / 100.0 for i in range(4))
+    hw, xcc = t[:, 4] & 0xFFFFFFFF, t[:, 4] >> 32
+    cu_key = list(zip(xcc.tolist(), ((hw >> 13) & 7).tolist(), ((hw >> 12) & 1).tolist(), ((hw >> 8) & 15).tolist()))
+    pct = lambda a: [round(float(v), 2) for v in np.percentile(a, [0, 10, 50, 90, 100])]
+    cus = collections.defaultdict(list)
+    for i, key in enumerate(cu_key):
+        cus[key].append(i)
+    gaps, rank = [], np.zeros(nwg, dtype=int)
+    for ids in cus.values():
+        ids.sort(key=lambda i: st[i])
+        for r, i in enumerate(ids):
+            rank[i] = r
+        gaps += [st[b] - en[a] for a, b in zip(ids, ids[1:])]
+    loop = lp - pro
+    per_cu_loop = np.array([loop[ids].sum() for ids in cus.values()])
+    per_cu_end = np.array([en[ids].max() for ids in cus.values()])
+    xcds = {}
+    for xc in sorted(set(xcc.tolist())):
+        keys = [k for k in cus if k[0] == xc]
+        xcds[int(xc)] = {"loop_sum_per_cu_mean": round(float(np.mean([loop[cus[k]].sum() for k in keys])), 2),
+                         "last_end": round(float(max(en[cus[k]].max() for k in keys)), 2)}
+    return {
+        "workload": w.name, "workgroups": int(nwg), "span_us": round(float(en.max()), 2),
+        "percentiles": "p0 p10 p50 p90 p100",
+        "start_offset": pct(st), "prologue": pct(pro - st), "main_loop": pct(loop), "o_store": pct(en - lp),
+        "end": pct(en),
+        "cus": len(cus), "workgroups_per_cu": dict(collections.Counter(len(v) for v in cus.values())),
+        "loop_sum_per_cu": pct(per_cu_loop), "last_end_per_cu": pct(per_cu_end),
+        "gap_between_workgroups_on_a_cu": pct(np.array(gaps)) if gaps else None,
+        "by_start_rank_on_cu": {int(r): {"main_loop_p50": round(float(np.median(loop[rank == r])), 2),
+                                         "end_p50": round(float(np.median(en[rank == r])), 2)}
+                                for r in range(rank.max() + 1)},
+        "xcd": xcds,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -647,6 +718,9 @@ def main():
                     help="write profiles/counters_<NAME>.txt from rocprofv3 --pmc passes over --workload")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--summary-prefix", default="kernel_trace", help="file name prefix of --summarize-trace")
+    ap.add_argument("--timeline", nargs="+", metavar="NAME",
+                    help="per-workgroup phase timeline of one forward launch of each workload, from the "
+                         "diagnostic build (python -m exact_io_aware_48_amd.build --timeline); one JSON line each")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -671,6 +745,13 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+
+    if args.timeline:
+        from exact_io_aware_48_amd import _lib
+        tl = _lib.load_timeline()
+        for name in args.timeline:
+            print(json.dumps(timeline_summary(by_name(name), tl)), flush=True)
+        return 0
 
     w = by_name(args.workload)
     if args.copy_calibration:

@@ -18,7 +18,20 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_48_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def load_timeline():
+    """The diagnostic timeline build (a separate library, loaded beside the
+    product one); raise if it has not been built."""
+    path = os.path.join(os.path.dirname(LIB_PATH), "libfa_fwd_timeline.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_48_amd.build --timeline`")
+    return _declare(ctypes.CDLL(path))
+
+
+def _declare(lib):
     vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]
     lib.fa_fwd.restype = i32
@@ -58,5 +71,6 @@ def load():
     lib.fa_lse_merge.restype = i32
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i32
-    _lib = lib
+    lib.fa_timeline_read.argtypes = [vp, i64]
+    lib.fa_timeline_read.restype = i32
     return lib

@@ -1,9 +1,11 @@
 """Build step: compile the HIP sources into the in-tree shared library.
 
-    python -m exact_io_aware_48_amd.build
+    python -m exact_io_aware_48_amd.build [--timeline]
 
-produces ``exact_io_aware_48_amd/libfa_fwd.so`` for gfx950.  It always
-recompiles (a build check must not trust a stale binary).
+produces ``exact_io_aware_48_amd/libfa_fwd.so`` for gfx950 (``--timeline``:
+the diagnostic build ``libfa_fwd_timeline.so``, whose forward kernels stamp
+their phases; see fa_timeline_read).  It always recompiles (a build check
+must not trust a stale binary).
 """
 
 import os
@@ -17,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_fwd.so")
+# diagnostic build with per-workgroup timeline stamps (-DFA_TIMELINE)
+LIB_TIMELINE = os.path.join(PKG, "libfa_fwd_timeline.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, f) for f in ("fa_api.hip", "fa_var_api.hip", "fa_bwd_api.hip", "fa_split_api.hip")]
@@ -52,24 +56,27 @@ def _run(cmd):
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
 
 
-def build(verbose=False, jobs=None):
-    """Compile every source (in parallel) and link the library."""
+def build(verbose=False, jobs=None, timeline=False):
+    """Compile every source (in parallel) and link the library (timeline=True:
+    the diagnostic timeline build, a separate file)."""
     from concurrent.futures import ThreadPoolExecutor
+    out = LIB_TIMELINE if timeline else LIB
+    extra = ["-DFA_TIMELINE"] if timeline else []
     tmpdir = tempfile.mkdtemp(prefix="fa_build_")
     try:
         objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in SOURCES]
         jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
         with ThreadPoolExecutor(max_workers=jobs) as pool:
-            list(pool.map(_run, [compile_cmd(src, obj) for src, obj in zip(SOURCES, objs)]))
-        tmp = LIB + ".tmp"
+            list(pool.map(_run, [compile_cmd(src, obj, extra) for src, obj in zip(SOURCES, objs)]))
+        tmp = out + ".tmp"
         _run(link_cmd(objs, tmp))
-        os.replace(tmp, LIB)
+        os.replace(tmp, out)
     finally:
         shutil.rmtree(tmpdir, ignore_errors=True)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, timeline="--timeline" in sys.argv[1:])

@@ -224,4 +224,18 @@ const char* fa_status_string(int status) {
 
 int fa_version(void) { return 100; }
 
+fa_status fa_timeline_read(void* dst, int64_t bytes) {
+#ifdef FA_TIMELINE
+  if (!dst) return FA_ERR_NULL;
+  if (bytes < 0 || bytes > (int64_t)sizeof(unsigned long long) * fa::kTimelineWords) return FA_ERR_SHAPE;
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(fa::fa_timeline_buf), (size_t)bytes, 0, hipMemcpyDeviceToHost) == hipSuccess
+             ? FA_OK
+             : FA_ERR_HIP;
+#else
+  (void)dst;
+  (void)bytes;
+  return FA_ERR_UNSUPPORTED;
+#endif
+}
+
 }  // extern "C"

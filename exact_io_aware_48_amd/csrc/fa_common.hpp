@@ -36,6 +36,43 @@ struct Params {
   int nb;                  // block-sparse: blocks per side, ceil(N / kMaskBlock)
 };
 
+// ---------------------------------------------------------------- timeline
+// Diagnostic builds (-DFA_TIMELINE, python -m exact_io_aware_48_amd.build
+// --timeline) stamp each forward workgroup's phases with the 100 MHz
+// s_memrealtime clock: entry, Q and first tiles in, main loop done, O
+// stored (after a workgroup barrier).  Thread 0 writes six words per
+// workgroup (the four stamps, XCC_ID << 32 | HW_ID, row block << 32 | head)
+// with plain vector stores; fa_timeline_read copies them out.  Product builds
+// compile all of it away.
+#ifdef FA_TIMELINE
+constexpr bool kTimeline = true;
+constexpr int kTimelineWords = 1 << 18;
+static __device__ unsigned long long fa_timeline_buf[kTimelineWords];
+#else
+constexpr bool kTimeline = false;
+#endif
+__device__ __forceinline__ unsigned long long timeline_clock() {
+  if constexpr (kTimeline) return __builtin_amdgcn_s_memrealtime();
+  return 0;
+}
+__device__ __forceinline__ void timeline_record(unsigned long long t0, unsigned long long t1, unsigned long long t2,
+                                                int bh, int rb) {
+#ifdef FA_TIMELINE
+  __syncthreads();
+  const unsigned long long t3 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0 && (blockIdx.x + 1) * 6 <= (unsigned)kTimelineWords) {
+    unsigned long long* w = fa_timeline_buf + blockIdx.x * 6;
+    const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_REG_HW_ID
+    const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // HW_REG_XCC_ID
+    w[0] = t0; w[1] = t1; w[2] = t2; w[3] = t3;
+    w[4] = ((unsigned long long)xcc << 32) | hw;
+    w[5] = ((unsigned long long)(unsigned)rb << 32) | (unsigned)bh;
+  }
+#else
+  (void)t0; (void)t1; (void)t2; (void)bh; (void)rb;
+#endif
+}
+
 enum { VAR_NONE = 0, VAR_ALIBI = 1, VAR_BLOCKSPARSE = 2 };
 constexpr int kMaskBlock = 128;   // block-sparse mask granularity (queries x keys)
 

@@ -108,6 +108,7 @@ template <int D, int BC, int NW, int MODE, bool CAUSAL, bool PP = false, int VAR
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_kernel(Params p) {
   static_assert(!(PRIO && RP), "one priority scheme");
+  const unsigned long long t_entry = timeline_clock();
   static_assert(VAR == VAR_NONE || !PP, "variants: no ping-pong");
   static_assert(VAR != VAR_BLOCKSPARSE || ((32 * NW) % kMaskBlock == 0 && kMaskBlock % BC == 0),
                 "row blocks and key tiles nest in the mask blocks");
@@ -300,6 +301,7 @@ void fa_fwd_kernel(Params p) {
     if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
   };
 
+  unsigned long long t_pro = 0;
   if constexpr (VAR == VAR_BLOCKSPARSE) {
     // ---------------- block-sparse: only the tiles some wave's block allows
     const uint8_t* mrow = p.bmask + (int64_t)(bh / p.H) * p.bm_sb + (int64_t)(bh % p.H) * p.bm_sh;
@@ -332,6 +334,7 @@ void fa_fwd_kernel(Params p) {
     if constexpr (DMA) wait_vmcnt<0>();
     __syncthreads();
     take_q();
+    t_pro = timeline_clock();
     int cur = 0;
     while (j < n_tiles) {
       const int jn = next_needed(j + 1);
@@ -367,6 +370,7 @@ void fa_fwd_kernel(Params p) {
     }
     __syncthreads();
     take_q();
+    t_pro = timeline_clock();
 
     if constexpr (!PP) {
       // two-slot ring: step j uses slot j % 2 and fills the other; unrolled
@@ -428,9 +432,11 @@ void fa_fwd_kernel(Params p) {
     }
   }
 
-  // (not at d = 256 for the block-sparse bf16 instances and the fp8 ones,
-  // where it costs spills)
-  constexpr bool O_STAGE = MODE != MODE_F32 && !(D == 256 && (MODE == MODE_FP8 || VAR == VAR_BLOCKSPARSE));
+  const unsigned long long t_loop = timeline_clock();
+  // (not at d = 256 for the block-sparse bf16 instances and the causal or
+  // variant fp8 ones, where it costs spills)
+  constexpr bool O_STAGE = MODE != MODE_F32 && !(D == 256 && ((MODE == MODE_BF16 && VAR == VAR_BLOCKSPARSE) ||
+                                                              (MODE == MODE_FP8 && (CAUSAL || VAR != VAR_NONE))));
   if constexpr (O_STAGE) {
     // every loop above ends with a barrier: the rings are free for O, whose
     // rows leave in whole segments (as many d-blocks per pass as a wave's
@@ -441,6 +447,7 @@ void fa_fwd_kernel(Params p) {
   } else {
     T::store(p, head_off, bh, my_q, ln, oacc, m_run, l_run);
   }
+  timeline_record(t_entry, t_pro, t_loop, bh, rb);
 }
 
 }  // namespace fa

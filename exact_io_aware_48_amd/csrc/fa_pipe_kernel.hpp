@@ -189,6 +189,7 @@ void fa_fwd_pipe_kernel(Params p) {
   using W = PipeWave<D, BC, NW>;
   constexpr int KB = W::KB, NDB = W::NDB;
   static_assert(G::KST == 2 && G::VST == 2, "two-slot K and V rings");
+  const unsigned long long t_entry = timeline_clock();
 
   // K and V rings, then the Q tile (prologue); the O tile reuses the rings
   constexpr int QTILEB = G::BR * T::QROWB;
@@ -259,6 +260,7 @@ void fa_fwd_pipe_kernel(Params p) {
     T::to_exponents(sa, c2, m_run);
   }
   __syncthreads();                                // every wave is done with K_0's slot
+  const unsigned long long t_pro = timeline_clock();
 
   // ---- main loop, unrolled by two so that ring slots and score buffers are fixed
   // iteration j: K_{j+1} in kslot((j+1)%2), V_j in vslot(j%2); fetch K_{j+2}
@@ -302,8 +304,10 @@ void fa_fwd_pipe_kernel(Params p) {
   }
   if (j < n_tiles) step(j, sa, sb, 0);
 
+  const unsigned long long t_loop = timeline_clock();
   // the last step ended with a barrier: the rings are free for the O tile
   T::template store_lds<NDB>(p, head_off, bh, qw0, my_q, ln, oacc, m_run, l_run, smem + wave * 32 * T::QROWB, lane);
+  timeline_record(t_entry, t_pro, t_loop, bh, rb);
 }
 
 }  // namespace fa

@@ -193,6 +193,21 @@ const char* fa_status_string(int status);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int fa_version(void);
 
+/*
+ * Diagnostic timeline of the last forward launch through fa_fwd, fa_fwd_fp8,
+ * fa_fwd_gqa or fa_fwd_gqa_fp8 on the current device (a measurement aid, not
+ * part of the attention computation).  Only a library built with
+ * -DFA_TIMELINE (python -m exact_io_aware_48_amd.build --timeline, a separate
+ * file) records it; any other build returns FA_ERR_UNSUPPORTED and touches
+ * nothing.  Per workgroup id w, six 64-bit words at dst[6w .. 6w+5]: the
+ * 100 MHz s_memrealtime stamps at entry, after its Q and first K/V tiles,
+ * after the main loop, and after the O store, then (XCC_ID << 32 | HW_ID) and
+ * (row block << 32 | batch*head).  bytes: how much to copy (at most 2 MiB);
+ * dst is host memory owned by the caller.  Synchronous with the device.
+ * FA_ERR_NULL for a NULL dst, FA_ERR_SHAPE for a size out of range.
+ */
+fa_status fa_timeline_read(void* dst, int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

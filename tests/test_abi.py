@@ -34,13 +34,20 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_alibi",
                                     "fa_fwd_alibi_fp8", "fa_fwd_blocksparse", "fa_fwd_blocksparse_fp8", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split",
                                     "fa_fwd_split_noalloc", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
-                                    "fa_split_scratch_bytes", "fa_status_string", "fa_version"]
+                                    "fa_split_scratch_bytes", "fa_status_string", "fa_timeline_read", "fa_version"]
 
 
 def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(lib._name)
     for name in declared_functions():
         assert hasattr(raw, name), name
+
+
+def test_timeline_read_is_unsupported_in_the_product_build(lib):
+    import numpy as np
+    buf = np.zeros(12, dtype=np.uint64)
+    assert lib.fa_timeline_read(buf.ctypes.data, buf.nbytes) == 3        # FA_ERR_UNSUPPORTED
+    assert not buf.any()
 
 
 def test_status_strings_and_version(lib):
