@@ -669,7 +669,9 @@ def timeline_summary(w, lib, launches=200):
         ids.sort(key=lambda i: st[i])
         for r, i in enumerate(ids):
             rank[i] = r
-        gaps += [st[b] - en[a] for a, b in zip(ids, ids[1:])]
+        # idle time between a workgroup's end and the start of the next on
+        # the CU (only where they ran one after another)
+        gaps += [st[b] - en[a] for a, b in zip(ids, ids[1:]) if st[b] >= en[a]]
     loop = lp - pro
     per_cu_loop = np.array([loop[ids].sum() for ids in cus.values()])
     per_cu_end = np.array([en[ids].max() for ids in cus.values()])
@@ -685,7 +687,7 @@ def timeline_summary(w, lib, launches=200):
         "end": pct(en),
         "cus": len(cus), "workgroups_per_cu": dict(collections.Counter(len(v) for v in cus.values())),
         "loop_sum_per_cu": pct(per_cu_loop), "last_end_per_cu": pct(per_cu_end),
-        "gap_between_workgroups_on_a_cu": pct(np.array(gaps)) if gaps else None,
+        "gap_between_sequential_workgroups_on_a_cu": pct(np.array(gaps)) if gaps else None,
         "by_start_rank_on_cu": {int(r): {"main_loop_p50": round(float(np.median(loop[rank == r])), 2),
                                          "end_p50": round(float(np.median(en[rank == r])), 2)}
                                 for r in range(rank.max() + 1)},
