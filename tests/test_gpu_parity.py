@@ -174,6 +174,35 @@ def test_running_max_grows_at_row_dependent_rates(dtype, d, causal):
     check(errors(o, ref, l, lref), dtype, f"row-dependent growth {dtype} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_jump_after_the_first_tiles(d, causal):
+    """From key J on, every score rises by a row-dependent amount, up to about
+    18 (natural units; 26 in log2 units) above the earlier keys: tiles after
+    a row's first take the exponentials against a base far below their
+    maximum, their lane sums pass the bound, and the tile is redone against a
+    new base for the rows that grew by more than the lag (others keep
+    theirs).  J differs per head so the jump falls at different tile phases."""
+    N = 700
+    w = by_name("bertl_bf16_b16h16n512d64").with_(B=1, H=3, N=N, d=d, causal=causal)
+    base = make_inputs(w.with_(dtype="f32"))
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = base.q * np.float32(0.5)
+    k = base.k * np.float32(0.5)
+    beta = np.linspace(0.0, 1.5, N, dtype=np.float32)              # per query row
+    alpha = np.float32(12.0 / (1.5 * w.softmax_scale))               # score rise 12 * beta: up to 18
+    for h, J in enumerate((70, 200, 333)):
+        q[0, h] += beta[:, None] * u[None, :] * np.float32(1.5)
+        k[0, h, J:] += alpha * u[None, :]
+    x = from_f32(w, q, k, base.v)
+    _print_case("jump", d, causal)
+    o, l = run_gpu(x)
+    ref, lref = oracle_full(x)
+    check(errors(o, ref, l, lref), "bf16", f"score jump d={d} causal={causal}")
+
+
 # ---------------------------------------------------------------- maximum sizes
 def _edge_rows(N, extra, seed):
     rng = np.random.default_rng(seed)
