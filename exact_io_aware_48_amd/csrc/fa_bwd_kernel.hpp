@@ -73,6 +73,17 @@ struct BwdParams {
 
 constexpr int kStatRows = 64;   // queries per statistics tile
 
+// vmcnt(0), written as inline asm (ordered with the DMA asm around it) and
+// again as the builtin, which the compiler's own wait insertion sees: it
+// does not see waits in inline asm, so registers loaded before a loop would
+// otherwise get a fresh vmcnt(0) at their first use inside it, one that also
+// waits for the prefetch DMA in flight.  Builtin immediate (gfx9 encoding):
+// vmcnt 0, expcnt 7 and lgkmcnt 15 (no wait on those).
+__device__ __forceinline__ void wait_vmcnt0_seen() {
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // Chunk swizzle for tiles read both row-wise (16 lanes x 16 rows at one
 // logical chunk, ds_read_b128) and transposed (32 lanes x 4 rows x 4 adjacent
 // chunks, ds_read_b64_tr_b16).  With RPP rows per 256-byte bank span and
@@ -292,28 +303,39 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int64_t bhq = (int64_t)bhk * p.qg + hp + (int64_t)ih * p.parts;
     stage.issue(static_cast<const char*>(p.q) + bhq * N * ROWB, t * BQ, N, dst, wave, lane);
     stage.issue(static_cast<const char*>(p.dout) + bhq * N * ROWB, t * BQ, N, dst + TILEB, wave, lane);
-    if (wave == 0) dma16(p.ws + (bhq * T + t) * (2 * kStatRows) + 4 * (lane & 31), dst + 2 * TILEB);
+    if (wave == 0)
+      dma16_s(reinterpret_cast<const char*>(p.ws + (bhq * T + t) * (2 * kStatRows)), 16 * (lane & 31), dst + 2 * TILEB);
   };
 
+  // Per-lane LDS offsets of the operand reads.  swz16 depends on row % 16
+  // only, and the chunk bits a read varies (4c in chunk 4c + g, 2db in chunk
+  // 2db + (lane & 3) / 2) are disjoint from the lane's own, so every offset
+  // is a lane base XOR a chunk term plus a constant row offset:
+  //   row_a, v_b: ra ^ (c << 6) + 16 * ROWB * (row block)
+  //   tr_a:       ta ^ (db << 5) + ROWB * (32 s, + 16 for the upper rows)
+  // The bases are re-laundered per tile (at its top), so the XORs are formed
+  // where they are used rather than kept live across the loop, where they
+  // spilled and every reload waited for the prefetch DMA in flight.
+  int ra = m * ROWB + ((g ^ swz16<CPR>(m)) << 4);
+  int ta;
+  {
+    const int r0 = 4 * g + ((lane >> 2) & 3);
+    ta = r0 * ROWB + (((((lane & 3) >> 1) ^ swz16<CPR>(r0)) << 4) | (8 * (lane & 1)));
+  }
   // A operand: rows 16*qb + m of a Q or dO tile, dims 32c + 8g .. +7
   auto row_a = [&](const char FA_LDS* base, int qb, int c) __attribute__((always_inline)) {
-    const int row = 16 * qb + m;
-    return __builtin_bit_cast(bf16x8, lds_read16(base + row * ROWB + (((4 * c + g) ^ swz16<CPR>(row)) << 4)));
+    return __builtin_bit_cast(bf16x8, lds_read16(base + 16 * qb * ROWB + (ra ^ (c << 6))));
   };
   // A operand X^T: dims 16*db + m over the queries of 32-query step s in k-slot order
   auto tr_a = [&](const char FA_LDS* base, int s, int db) __attribute__((always_inline)) {
-    const int row = 32 * s + 4 * g + ((lane >> 2) & 3);
-    const int col = 32 * db + 8 * (lane & 3);   // bytes
-    const int off0 = row * ROWB + ((((col >> 4) ^ swz16<CPR>(row)) << 4) | (col & 15));
-    const int off1 = (row + 16) * ROWB + ((((col >> 4) ^ swz16<CPR>(row + 16)) << 4) | (col & 15));
-    const i16x4 lo = lds_tr16(base + off0), hi = lds_tr16(base + off1);
+    const char FA_LDS* b = base + 32 * s * ROWB + (ta ^ (db << 5));
+    const i16x4 lo = lds_tr16(b), hi = lds_tr16(b + 16 * ROWB);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   // B operand V^T: keys KW*wave + 16*kb + m, dims 32c + 8g .. +7
   auto v_b = [&](int kb, int c) __attribute__((always_inline)) {
     if constexpr (VLDS) {
-      const int row = KW * wave + 16 * kb + m;
-      return __builtin_bit_cast(bf16x8, lds_read16(vsm + row * ROWB + (((4 * c + g) ^ swz16<CPR>(row)) << 4)));
+      return __builtin_bit_cast(bf16x8, lds_read16(vsm + (KW * wave + 16 * kb) * ROWB + (ra ^ (c << 6))));
     } else {
       return vf[kb][c];
     }
@@ -324,6 +346,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int ih = it / nt, t = t0 + it - ih * nt;
     const int qt0 = t * BQ;
     if (CAUSAL && qt0 + BQ - 1 < kw0) return;          // every query of the tile precedes every key of the wave
+    asm volatile("" : "+v"(ra), "+v"(ta));
     const char FA_LDS* dos = qs + TILEB;
     const char FA_LDS* st = qs + 2 * TILEB;
     const bool diag = CAUSAL && qt0 < kw0 + KW - 1;
@@ -391,7 +414,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     vstage.issue(static_cast<const char*>(p.v) + kv_off * 2, k0, N, vsm, wave, lane);
   }
   issue(0, slot(0));
-  wait_vmcnt<0>();
+  wait_vmcnt0_seen();   // K and V registers, Q/dO tile 0
   __syncthreads();
   if constexpr (CAUSAL) {
     // two-slot ring, unrolled by two so that the slot offsets are constants
