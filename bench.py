@@ -84,12 +84,16 @@ KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48
                   "exact_io_aware_48_amd/csrc/fa_fwd_kernel.hpp", "exact_io_aware_48_amd/csrc/fa_pipe_kernel.hpp",
                   "exact_io_aware_48_amd/csrc/fa_host.hpp", "exact_io_aware_48_amd/csrc/fa_launch.hpp",
                   "exact_io_aware_48_amd/csrc/fa_api.hip", "include/fa_fwd.h"]
+# sources of the backward kernels (hashed into the backward trace summaries)
+BWD_KERNEL_SOURCES = ["exact_io_aware_48_amd/csrc/fa_common.hpp", "exact_io_aware_48_amd/csrc/fa_host.hpp",
+                      "exact_io_aware_48_amd/csrc/fa_bwd_kernel.hpp", "exact_io_aware_48_amd/csrc/fa_bwd_api.hip",
+                      "include/fa_bwd.h"]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -578,9 +582,11 @@ def summarize_trace(trace_dir, workload_name, command, prefix="kernel_trace"):
     for fn in files:
         with open(fn) as f:
             rows += list(csv.DictReader(f))
+    backward = prefix.startswith("kernel_trace_backward")
     lines = [f"rocprofv3 kernel statistics: {workload_name}",
              f"command: {command}",
-             f"kernel sources sha: {kernel_source_hash()}",
+             (f"backward kernel sources sha: {kernel_source_hash(BWD_KERNEL_SOURCES)}" if backward else
+              f"kernel sources sha: {kernel_source_hash()}"),
              "",
              f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share%':>7s}"]
     for r in rows:

@@ -68,6 +68,20 @@ def test_summarize_trace_writes_the_kernel_table(tmp_path, monkeypatch):
     assert f"kernel sources sha: {bench.kernel_source_hash()}" in text
 
 
+def test_backward_trace_summary_hashes_the_backward_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    d = tmp_path / "trace"
+    d.mkdir()
+    (d / "kt_kernel_stats.csv").write_text(
+        "Name,Calls,TotalDurationNs,AverageNs,Percentage,MinNs,MaxNs\n"
+        "\"void fa::fa_bwd_dq_kernel<64, 64, 4, 2, true>(fa::BwdParams)\",10,300000,30000,100.0,29000,36000\n")
+    bench.summarize_trace(str(d), "gpt2s_causal_bf16_b8h12n1024d64", "cmd", "kernel_trace_backward")
+    text = (tmp_path / "profiles" / "kernel_trace_backward_gpt2s_causal_bf16_b8h12n1024d64.txt").read_text()
+    sha = bench.kernel_source_hash(bench.BWD_KERNEL_SOURCES)
+    assert f"backward kernel sources sha: {sha}" in text and sha != bench.kernel_source_hash()
+    assert all(os.path.exists(os.path.join(bench.ROOT, rel)) for rel in bench.BWD_KERNEL_SOURCES)
+
+
 def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
     name = "gpt2s_causal_bf16_b8h12n1024d64"
