@@ -40,8 +40,8 @@ It also carries ``variants``: ALiBi on the long-context and GPT-2-small
 workloads (TFLOP/s by the plain convention) and a block-sparse sliding
 window with one global block (TFLOP/s over the allowed query/key pairs,
 and the speed-up over the dense kernel).  And ``decode``: one fa_fwd_split call (split kernel and merge) on
-the decode workloads, as HBM bandwidth over the compulsory bytes (K and V
-read once) against the 8 TB/s peak.  ``cold``: the GPT-2- and BERT-shaped
+the decode workloads (fa_fwd_split_fp8 for the one with an fp8 K/V cache), as
+HBM bandwidth over the compulsory bytes (K and V read once) against the 8 TB/s peak.  ``cold``: the GPT-2- and BERT-shaped
 forward workloads (whose inputs fit in the 256 MiB MALL) timed with a 512 MiB
 device write before every launch, p10/p50/p90 of single launches.  ``gpu``:
 the device name, architecture and compute units, and the current clock
@@ -181,15 +181,22 @@ def time_backward(w, steps, warmup, settle_s=0.25, graph=False):
 
 
 def time_decode(w, steps, warmup, settle_s=0.25, graph=False):
-    """Time exactly `steps` calls of fa_fwd_split (split kernel + merge) on decode workload w."""
+    """Time exactly `steps` calls of fa_fwd_split, or fa_fwd_split_fp8 on fp8 inputs (split
+    kernel + merge), on decode workload w."""
     import torch
     import exact_io_aware_48_amd as fa
-    _, q, k, v = device_inputs(w)
-    splits, nbytes = fa.fa_fwd_split_plan(w.B, w.H, w.kv_heads, w.q_rows, w.N, w.d, 0)
+    x, q, k, v = device_inputs(w)
+    fp8 = w.dtype == "fp8"
+    splits, nbytes = fa.fa_fwd_split_plan(w.B, w.H, w.kv_heads, w.q_rows, w.N, w.d, 0, fp8=fp8)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((w.B, w.H, w.q_rows), dtype=torch.float32, device="cuda")
-    launch = lambda: fa.fa_fwd_split(q, k, v, scale=w.softmax_scale, causal=w.causal, o=o, lse=lse, workspace=ws)
+    if fp8:
+        launch = lambda: fa.fa_fwd_split_fp8(q, k, v, *x.descale, scale=w.softmax_scale, causal=w.causal, o=o,
+                                             lse=lse, workspace=ws)
+    else:
+        launch = lambda: fa.fa_fwd_split(q, k, v, scale=w.softmax_scale, causal=w.causal, o=o, lse=lse,
+                                         workspace=ws)
     t = time_launch(launch, steps, warmup, settle_s, graph)
     t["splits"] = splits
     return t
@@ -851,7 +858,7 @@ def main():
         for dw in DECODE_WORKLOADS:
             dt = time_decode(dw, None, max(5, args.warmup), args.settle, graph=args.graph)
             gbs = dw.compulsory_bytes / (dt["kernel_ms_mean"] * 1e-3) / 1e9
-            dec[dw.name] = {"us_per_call": round(dt["kernel_ms_mean"] * 1e3, 1), "splits": dt["splits"],
+            dec[dw.name] = {"us_per_call": round(dt["kernel_ms_mean"] * 1e3, 1), "splits": dt["splits"], "dtype": dw.dtype,
                             "hbm_gbs": round(gbs, 0), "frac_of_hbm_peak": round(gbs / HBM_GBPS, 4),
                             "compulsory_bytes": dw.compulsory_bytes,
                             "launches": "split kernel, merge"}

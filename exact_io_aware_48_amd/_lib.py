@@ -63,6 +63,9 @@ def _declare(lib):
     lib.fa_fwd_split_plan.restype = i32
     lib.fa_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.fa_fwd_split.restype = i32
+    lib.fa_fwd_split_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, f32, f32, i32, i32,
+                                     vp]
+    lib.fa_fwd_split_fp8.restype = i32
     lib.fa_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, i32, i32, i32, vp]
     lib.fa_fwd_split_noalloc.restype = i32
     lib.fa_split_scratch_bytes.argtypes = []

@@ -351,10 +351,11 @@ def fa_bwd(q, k, v, o, do, lse, scale=None, causal=False, dq=None, dk=None, dv=N
     return dq, dk, dv
 
 
-def fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, num_splits=0):
-    """(splits, workspace bytes) fa_fwd_split would use."""
+def fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, num_splits=0, fp8=False):
+    """(splits, workspace bytes) fa_fwd_split (fa_fwd_split_fp8 when fp8) would use."""
     sp, nb = ctypes.c_int(), ctypes.c_int64()
-    st = _lib.load().fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, int(num_splits), _lib.FA_BF16, ctypes.byref(sp),
+    dtype = _lib.FA_FP8_E4M3 if fp8 else _lib.FA_BF16
+    st = _lib.load().fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, int(num_splits), dtype, ctypes.byref(sp),
                                        ctypes.byref(nb))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_split_plan")
@@ -383,6 +384,32 @@ def fa_fwd_split(q, k, v, scale=None, causal=False, num_splits=0, o=None, lse=No
                                   int(num_splits), _lib.FA_BF16, _stream_ptr(stream))
     if st != _lib.FA_OK:
         raise FaError(st, "fa_fwd_split")
+    return o, lse
+
+
+def fa_fwd_split_fp8(q8, k8, v8, q_descale, k_descale, v_descale, scale=None, causal=False, num_splits=0, o=None,
+                     lse=None, workspace=None, stream=None):
+    """fa_fwd_split on FP8 (OCP e4m3fn) inputs with per-tensor descales: q8 [B, H, N_q, d],
+    k8 and v8 [B, H_kv, N_k, d].  Returns (o, lse): bfloat16 [B, H, N_q, d] and float32 [B, H, N_q]."""
+    for t, nm in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _check(t, nm)
+        if t.dtype not in _FP8_DTYPES:
+            raise ValueError(f"{nm} must be float8_e4m3fn or uint8 bytes")
+    B, H, N_q, d = q8.shape
+    if k8.shape != v8.shape or k8.shape[0] != B or k8.shape[3] != d:
+        raise ValueError("k8 and v8 must both be [B, H_kv, N_k, d] with q8's B and d")
+    H_kv, N_k = k8.shape[1], k8.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _, need = fa_fwd_split_plan(B, H, H_kv, N_q, N_k, d, num_splits, fp8=True)
+    workspace = _workspace(workspace, need, q8.device)
+    o, lse = _outputs(o, lse, q8.shape, torch.bfloat16, (B, H, N_q), q8.device)
+    st = _lib.load().fa_fwd_split_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      workspace.data_ptr(), B, H, H_kv, N_q, N_k, d, float(scale), float(q_descale),
+                                      float(k_descale), float(v_descale), int(bool(causal)), int(num_splits),
+                                      _stream_ptr(stream))
+    if st != _lib.FA_OK:
+        raise FaError(st, "fa_fwd_split_fp8")
     return o, lse
 
 

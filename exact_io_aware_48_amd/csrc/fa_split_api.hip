@@ -53,9 +53,11 @@ void* scratch_on_current_device() {
 // Keys per tile per head dim: one wave per workgroup, 32 KiB of K/V ring at
 // d = 64 and 128, so that five workgroups share a CU and keep enough of the
 // K/V stream in flight.  d = 256 takes the smallest tile the 32 x 32 MFMA
-// allows (32 keys), a 64 KiB ring and two workgroups per CU.
-constexpr int split_bc_of(int d) { return d == 64 ? 64 : 32; }
-int split_bc(int64_t d) { return split_bc_of((int)d); }
+// allows (32 keys), a 64 KiB ring and two workgroups per CU.  fp8 takes
+// 64-key tiles at every d (its P V MFMA consumes 64 keys), which at one byte
+// per element gives the same ring sizes (16, 32 and 64 KiB).
+constexpr int split_bc_of(int d, bool fp8) { return fp8 || d == 64 ? 64 : 32; }
+int split_bc(int64_t d, int dtype) { return split_bc_of((int)d, dtype == FA_FP8_E4M3); }
 constexpr int kSplitNW = 1;
 constexpr int kRowsPerBlock = 32 * kSplitNW;
 
@@ -78,7 +80,7 @@ int device_cus() {
 }
 
 fa_status check_split_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int dtype) {
-  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || N_q < 1 || N_k < N_q) return FA_ERR_SHAPE;
   if (B > INT_MAX / H) return FA_ERR_SHAPE;
@@ -94,9 +96,9 @@ fa_status check_split_shape(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int
 // N_k = 32K takes 8; B = 4, H = 32, N_k = 16K takes 4), each split keeping at
 // least four tiles.
 fa_status make_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, int num_splits,
-                    int cus, Plan* out) {
+                    int dtype, int cus, Plan* out) {
   if (num_splits < 0) return FA_ERR_SHAPE;
-  const int64_t bc = split_bc(d);
+  const int64_t bc = split_bc(d, dtype);
   Plan pl{};
   pl.rows_per_head = (H / H_kv) * N_q;
   pl.nrb = (pl.rows_per_head + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -124,10 +126,10 @@ fa_status make_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k
 // plain double buffer is kept.
 constexpr int kSplitNS = 2;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int MODE>
 hipError_t launch_split(const SplitParams& p, int grid, hipStream_t stream) {
-  constexpr int BC = split_bc_of(D);
-  void (*kern)(SplitParams) = &fa::fa_split_kernel<D, BC, kSplitNW, kSplitNS, CAUSAL>;
+  constexpr int BC = split_bc_of(D, MODE == fa::MODE_FP8);
+  void (*kern)(SplitParams) = &fa::fa_split_kernel<D, BC, kSplitNW, kSplitNS, CAUSAL, MODE>;
   SplitParams args = p;
   void* kargs[] = {&args};
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(grid), dim3(64 * kSplitNW), kargs, 0, stream);
@@ -158,7 +160,7 @@ fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int
   fa_status st = check_split_shape(B, H, H_kv, N_q, N_k, d, dtype);
   if (st != FA_OK) return st;
   Plan pl;
-  st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, num_splits == 0 ? device_cus() : 256, &pl);
+  st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, dtype, num_splits == 0 ? device_cus() : 256, &pl);
   if (st != FA_OK) return st;
   if (splits) *splits = (int)pl.splits;
   if (workspace_bytes) *workspace_bytes = pl.workspace_bytes;
@@ -169,11 +171,19 @@ fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int
 
 namespace {
 
-// fa_fwd_split with the partials either in the caller's workspace or, when
+template <int MODE>
+hipError_t launch_split_mode(const SplitParams& p, int64_t d, bool causal, int grid, hipStream_t s) {
+  if (d == 64) return causal ? launch_split<64, true, MODE>(p, grid, s) : launch_split<64, false, MODE>(p, grid, s);
+  if (d == 128) return causal ? launch_split<128, true, MODE>(p, grid, s) : launch_split<128, false, MODE>(p, grid, s);
+  return causal ? launch_split<256, true, MODE>(p, grid, s) : launch_split<256, false, MODE>(p, grid, s);
+}
+
+// fa_fwd_split (and fa_fwd_split_fp8, dtype FA_FP8_E4M3 with the three
+// descales) with the partials either in the caller's workspace or, when
 // workspace is NULL, in `scratch` (fa_fwd_split_noalloc)
 fa_status run_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int64_t B,
                     int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
-                    int num_splits, int dtype, void* stream) {
+                    int num_splits, int dtype, void* stream, float dq = 1.f, float dk = 1.f, float dv = 1.f) {
   const bool use_scratch = workspace == nullptr;
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   fa_status st = check_split_shape(B, H, H_kv, N_q, N_k, d, dtype);
@@ -182,10 +192,13 @@ fa_status run_split(const void* q, const void* k, const void* v, void* o, float*
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
   if (!use_scratch && !aligned16(workspace)) return FA_ERR_ALIGN;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
-  const double c2 = std::fabs((double)scale) * 1.4426950408889634;
+  for (float ds : {dq, dk, dv})
+    if (!std::isfinite(ds) || !(ds > 0.f)) return FA_ERR_SCALE;
+  const bool fp8 = dtype == FA_FP8_E4M3;
+  const double c2 = std::fabs((double)scale) * (double)dq * (double)dk * 1.4426950408889634;
   if (!std::isfinite((float)c2)) return FA_ERR_SCALE;
   Plan pl;
-  st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, num_splits == 0 ? device_cus() : 256, &pl);
+  st = make_plan(B, H, H_kv, N_q, N_k, d, num_splits, dtype, num_splits == 0 ? device_cus() : 256, &pl);
   if (st != FA_OK) return st;
   if (use_scratch) {
     if (pl.workspace_bytes > kScratchBytes) return FA_ERR_SCRATCH;
@@ -208,15 +221,14 @@ fa_status run_split(const void* q, const void* k, const void* v, void* o, float*
   p.chunk = (int)pl.chunk;
   // masked scores are -inf and rely on c2 > 0 (see fa_api.hip); a negative scale flips Q's sign bits
   p.c2 = std::max((float)c2, 1e-30f);
-  p.qsign = scale < 0.f ? 0x80008000u : 0u;
+  p.out_mul = fp8 ? dv : 1.f;
+  p.qsign = scale < 0.f ? (fp8 ? 0x80808080u : 0x80008000u) : 0u;
   const int grid = (int)(pl.splits * pl.nrb * B * H_kv);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (d == 64) e = causal ? launch_split<64, true>(p, grid, s) : launch_split<64, false>(p, grid, s);
-  else if (d == 128) e = causal ? launch_split<128, true>(p, grid, s) : launch_split<128, false>(p, grid, s);
-  else e = causal ? launch_split<256, true>(p, grid, s) : launch_split<256, false>(p, grid, s);
-  if (e != hipSuccess) return FA_ERR_HIP;
-  e = launch_merge(p.o_part, p.lse_part, pl.splits, rows_total, d, o, lse, true, s);
+  const hipError_t e0 = fp8 ? launch_split_mode<fa::MODE_FP8>(p, d, causal != 0, grid, s)
+                            : launch_split_mode<fa::MODE_BF16>(p, d, causal != 0, grid, s);
+  if (e0 != hipSuccess) return FA_ERR_HIP;
+  const hipError_t e = launch_merge(p.o_part, p.lse_part, pl.splits, rows_total, d, o, lse, true, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -228,12 +240,23 @@ fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, flo
                        int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
                        int num_splits, int dtype, void* stream) {
   if (!workspace) return FA_ERR_NULL;
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   return run_split(q, k, v, o, lse, workspace, B, H, H_kv, N_q, N_k, d, scale, causal, num_splits, dtype, stream);
+}
+
+fa_status fa_fwd_split_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, void* workspace,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale,
+                           float q_descale, float k_descale, float v_descale, int causal, int num_splits,
+                           void* stream) {
+  if (!workspace) return FA_ERR_NULL;
+  return run_split(q8, k8, v8, o_bf16, lse, workspace, B, H, H_kv, N_q, N_k, d, scale, causal, num_splits,
+                   FA_FP8_E4M3, stream, q_descale, k_descale, v_descale);
 }
 
 fa_status fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                                int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale, int causal,
                                int num_splits, int dtype, void* stream) {
+  if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
   return run_split(q, k, v, o, lse, nullptr, B, H, H_kv, N_q, N_k, d, scale, causal, num_splits, dtype, stream);
 }
 

@@ -10,7 +10,9 @@
 // sequence too short in queries to fill the GPU.
 //
 // How:
-//   1. fa_split_kernel: a workgroup owns one key range (a split) of one K/V
+//   1. fa_split_kernel (bf16, or fp8 with per-tensor descales: the forward's
+//      fp8 pieces, e4m3 operands on the fp8 MFMA, P pre-scaled to e4m3):
+//      a workgroup owns one key range (a split) of one K/V
 //      head and up to 32*NW of its rows, a row being (query head of the
 //      group, query): decode has G * N_q rows per K/V head, so the query
 //      heads that share a K/V stream share one pass over it.  The range's
@@ -28,8 +30,8 @@
 namespace fa {
 
 struct SplitParams {
-  const void* q;      // bf16 [B][H][N_q][D]
-  const void* k;      // bf16 [B][H_kv][N_k][D]
+  const void* q;      // bf16 or e4m3 [B][H][N_q][D]
+  const void* k;      // bf16 or e4m3 [B][H_kv][N_k][D]
   const void* v;
   float* o_part;      // [S][B*H*N_q][D]
   float* lse_part;    // [S][B*H*N_q]
@@ -40,8 +42,9 @@ struct SplitParams {
   int nrb;            // row blocks per K/V head
   int S;              // splits
   int chunk;          // keys per split, a multiple of the tile
-  float c2;           // |scale| * log2(e)
+  float c2;           // |scale| * log2(e) (fp8: times the q and k descales)
   uint32_t qsign;     // XOR mask on Q's sign bits (negative scale)
+  float out_mul;      // fp8: the v descale (unused for bf16)
 };
 
 // Wait until the oldest tile in flight has landed, `more` being how many
@@ -59,9 +62,9 @@ __device__ __forceinline__ void wait_tile(int more) {
 }
 
 // NS: depth of the K/V ring (tiles j+1 .. j+NS-1 in flight while tile j is used).
-template <int D, int BC, int NW, int NS, bool CAUSAL>
+template <int D, int BC, int NW, int NS, bool CAUSAL, int MODE = MODE_BF16>
 __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
-  constexpr int MODE = MODE_BF16;
+  static_assert(MODE == MODE_BF16 || MODE == MODE_FP8, "bf16 or fp8 inputs");
   using G = Geo<D, BC, NW, MODE>;
   using T = Tile<D, BC, NW, MODE>;
   constexpr int NDB = T::NDB;
@@ -90,15 +93,22 @@ __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
   const bool row_ok = r < p.rows;
   const int hh = row_ok ? r / p.N_q : 0, qi = row_ok ? r - hh * p.N_q : 0;
   const int64_t row_g = (int64_t)bhk * p.rows + r;              // = (bhk*G + hh)*N_q + qi
+  // the row's Q slice as the B operand (bf16: dims 16c + 8hf .. +7 of step c;
+  // fp8: bytes 64c + 32hf .. +31)
   typename T::QFrag q;
   {
     const int sgn = (int)p.qsign;
-    const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + row_g * D);
+    const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const char*>(p.q) + row_g * G::ROWB);
+    const i32x4 sg{sgn, sgn, sgn, sgn}, zero{0, 0, 0, 0};
 #pragma unroll
     for (int c = 0; c < T::QK_STEPS; ++c) {
-      i32x4 w = row_ok ? src[2 * c + ln.hf] : i32x4{0, 0, 0, 0};
-      w ^= i32x4{sgn, sgn, sgn, sgn};
-      q.a[c] = __builtin_bit_cast(bf16x8, w);
+      if constexpr (MODE == MODE_FP8) {
+        const i32x4 w0 = (row_ok ? src[4 * c + 2 * ln.hf] : zero) ^ sg;
+        const i32x4 w1 = (row_ok ? src[4 * c + 2 * ln.hf + 1] : zero) ^ sg;
+        q.f8[c] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      } else {
+        q.a[c] = __builtin_bit_cast(bf16x8, (row_ok ? src[2 * c + ln.hf] : zero) ^ sg);
+      }
     }
   }
 
@@ -113,8 +123,8 @@ __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
   Stager<D, BC, NW, MODE, true> vstage;
   kstage.init(wave, lane);
   vstage.init(wave, lane);
-  const char* kglob = static_cast<const char*>(p.k) + kv_off * 2;
-  const char* vglob = static_cast<const char*>(p.v) + kv_off * 2;
+  const char* kglob = static_cast<const char*>(p.k) + kv_off * G::EB;
+  const char* vglob = static_cast<const char*>(p.v) + kv_off * G::EB;
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -177,8 +187,10 @@ __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
   if (!row_ok) return;
   const int64_t prow = (int64_t)s * p.BHkv * p.rows + row_g;   // row of this split's partial
   const bool seen = l_tot > 0.f;
-  const float inv = seen ? 1.f / l_tot : 0.f;
-  if (ln.hf == 0) p.lse_part[prow] = seen ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // fp8: l and O carry the pre-scale 2^EXP_SHIFT of P, which cancels in O / l
+  // and leaves L through the base
+  const float inv = seen ? (MODE == MODE_FP8 ? p.out_mul : 1.f) / l_tot : 0.f;
+  if (ln.hf == 0) p.lse_part[prow] = seen ? (m_run - T::EXP_SHIFT + __log2f(l_tot)) * kLn2 : -INFINITY;
   float* dst = p.o_part + prow * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

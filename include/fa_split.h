@@ -37,13 +37,15 @@ extern "C" {
 #endif
 
 /*
- * fa_fwd_split_plan -- the split count fa_fwd_split would use and the
- * workspace it needs (splits * B * H * N_q * (d + 1) * 4 bytes), without
- * launching anything.  num_splits = 0 lets the library choose (about two
- * workgroups per compute unit of the current device, at least four 32- or
- * 64-key tiles per split); a positive value asks for that many splits, fewer
- * when the key tiles run out.  splits and workspace_bytes may be NULL.
- * Checks as fa_fwd_split (FA_ERR_SHAPE also for num_splits < 0).
+ * fa_fwd_split_plan -- the split count fa_fwd_split (dtype FA_BF16) or
+ * fa_fwd_split_fp8 (dtype FA_FP8_E4M3) would use and the workspace it needs
+ * (splits * B * H * N_q * (d + 1) * 4 bytes), without launching anything.
+ * num_splits = 0 lets the library choose (about two workgroups per compute
+ * unit of the current device, at least four key tiles per split: 32 keys at
+ * d = 128 and 256 in bf16, else 64); a positive value asks for that many
+ * splits, fewer when the key tiles run out.  splits and workspace_bytes may
+ * be NULL.  Checks as fa_fwd_split (FA_ERR_SHAPE also for num_splits < 0;
+ * FA_ERR_UNSUPPORTED for a dtype other than those two).
  */
 fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d,
                             int num_splits, int dtype, int* splits, int64_t* workspace_bytes);
@@ -66,6 +68,31 @@ fa_status fa_fwd_split_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int
 fa_status fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                        int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d,
                        float scale, int causal, int num_splits, int dtype, void* stream);
+
+/*
+ * fa_fwd_split_fp8 -- fa_fwd_split on FP8 inputs with per-tensor scales, as
+ * fa_fwd_fp8 is the forward on them (the FP8 forward the pages attribute to
+ * FlashAttention-3: systems-analysis page section "FlashAttention-3 (2024)",
+ * glossary "Flash Attention 3 (Hopper)" paragraph, dexblog.ro table row on
+ * data types); for decoding this is an fp8 K/V cache, half the bytes of the
+ * bf16 stream the split pass is bound by.
+ *   q8         : OCP e4m3fn bytes [B][H][N_q][d]
+ *   k8, v8     : OCP e4m3fn bytes [B][H_kv][N_k][d]; the value of an element
+ *                is e4m3(x8) * x_descale
+ *   o_bf16     : bfloat16 output [B][H][N_q][d]
+ *   lse        : float32 output [B][H][N_q], natural-log logsumexp of the
+ *                scaled, dequantised scores
+ *   workspace  : the size fa_fwd_split_plan reports with dtype FA_FP8_E4M3
+ *   *_descale  : finite and > 0, else FA_ERR_SCALE
+ * Shapes, splits, the causal rule and the other errors as fa_fwd_split.
+ * Products and softmax statistics accumulate in float32, and the
+ * probabilities enter the P V product as in fa_fwd_fp8 (pre-scaled by 2^6,
+ * rounded to e4m3; the row sums use them unrounded).
+ */
+fa_status fa_fwd_split_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse, void* workspace,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k, int64_t d, float scale,
+                           float q_descale, float k_descale, float v_descale, int causal, int num_splits,
+                           void* stream);
 
 /*
  * fa_fwd_split_noalloc -- fa_fwd_split without a workspace argument, for

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_alibi",
                                     "fa_fwd_alibi_fp8", "fa_fwd_blocksparse", "fa_fwd_blocksparse_fp8", "fa_fwd_fp8", "fa_fwd_gqa", "fa_fwd_gqa_fp8", "fa_fwd_split",
-                                    "fa_fwd_split_noalloc", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
+                                    "fa_fwd_split_fp8", "fa_fwd_split_noalloc", "fa_fwd_split_plan", "fa_lse_merge", "fa_plan",
                                     "fa_split_scratch_bytes", "fa_status_string", "fa_timeline_read", "fa_version"]
 
 
@@ -192,9 +192,21 @@ def test_fa_fwd_split_plan(lib):
     assert st == 0 and sp == 4 and nb == 4 * 8 * 257 * 4
 
 
+def test_fa_fwd_split_plan_fp8_takes_64_key_tiles(lib):
+    # 100 keys at d = 128: four 32-key bf16 tiles, two 64-key fp8 tiles
+    assert _plan(lib, 1, 4, 4, 1, 100, 128, 50)[:2] == (0, 4)
+    assert _plan(lib, 1, 4, 4, 1, 100, 128, 50, dtype=2)[:2] == (0, 2)
+    # 8192 keys asked in 8 splits: 1024 keys each either way, and the same fp32 partials
+    assert _plan(lib, 2, 32, 8, 1, 8192, 128, 8, dtype=2) == _plan(lib, 2, 32, 8, 1, 8192, 128, 8)
+    # 640 keys at d = 64 over 3 splits: ten 64-key tiles in chunks of 4 for both dtypes
+    assert _plan(lib, 1, 1, 1, 1, 640, 64, 3, dtype=2)[:2] == (0, 3)
+    assert _plan(lib, 1, 4, 4, 1, 100, 256, 0, dtype=2)[:2] == (0, 1)
+
+
 @pytest.mark.parametrize("args,expected", [
     ((1, 8, 3, 1, 64, 64, 0), 2), ((1, 8, 8, 0, 64, 64, 0), 2), ((1, 8, 8, 65, 64, 64, 0), 2),
     ((1, 8, 8, 1, 64, 64, -1), 2), ((1, 8, 8, 1, 64, 512, 0), 3), ((1, 8, 8, 1, 64, 64, 0, 0), 3),
+    ((1, 8, 8, 1, 64, 64, 0, 3), 3), ((1, 8, 8, 1, 64, 96, 0, 2), 3), ((1, 8, 3, 1, 64, 64, 0, 2), 2),
 ])
 def test_fa_fwd_split_plan_validation(lib, args, expected):
     assert _plan(lib, *args)[0] == expected
@@ -202,7 +214,7 @@ def test_fa_fwd_split_plan_validation(lib, args, expected):
 
 @pytest.mark.parametrize("kw,expected", [
     ({"q": 0}, 1), ({"ws": 0}, 1), ({"N_q": 5, "N_k": 4}, 2), ({"H_kv": 3}, 2), ({"d": 512}, 3), ({"dtype": 0}, 3),
-    ({"o": FAKE + 2}, 4), ({"ws": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
+    ({"dtype": 2}, 3), ({"o": FAKE + 2}, 4), ({"ws": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
 ])
 def test_fa_fwd_split_validation(lib, kw, expected):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, B=1, H=4, H_kv=2, N_q=1, N_k=64, d=64, scale=0.1,
@@ -211,6 +223,21 @@ def test_fa_fwd_split_validation(lib, kw, expected):
     args = [a[n] for n in ("q", "k", "v", "o", "lse", "ws", "B", "H", "H_kv", "N_q", "N_k", "d", "scale", "causal",
                            "splits", "dtype")] + [None]
     assert lib.fa_fwd_split(*args) == expected
+
+
+@pytest.mark.parametrize("kw,expected", [
+    ({"q": 0}, 1), ({"v": 0}, 1), ({"ws": 0}, 1), ({"N_q": 5, "N_k": 4}, 2), ({"H_kv": 3}, 2), ({"B": 0}, 2),
+    ({"d": 512}, 3), ({"d": 96}, 3), ({"k": FAKE + 1}, 4), ({"ws": FAKE + 8}, 4), ({"scale": float("nan")}, 5),
+    ({"dq": 0.0}, 5), ({"dk": -1.0}, 5), ({"dv": float("inf")}, 5), ({"dq": float("nan")}, 5),
+    ({"scale": 3e38, "dq": 1e3}, 5),
+])
+def test_fa_fwd_split_fp8_validation(lib, kw, expected):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, B=1, H=4, H_kv=2, N_q=1, N_k=64, d=64, scale=0.1,
+             dq=1.0, dk=1.0, dv=1.0, causal=0, splits=0)
+    a.update(kw)
+    args = [a[n] for n in ("q", "k", "v", "o", "lse", "ws", "B", "H", "H_kv", "N_q", "N_k", "d", "scale", "dq", "dk",
+                           "dv", "causal", "splits")] + [None]
+    assert lib.fa_fwd_split_fp8(*args) == expected
 
 
 @pytest.mark.parametrize("args,expected", [
@@ -289,5 +316,7 @@ def test_split_noalloc_rejects_oversized_requests_before_any_launch(lib):
     assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 2, 1, 128, 0.1, 1, 0, 1, None) == 2
     assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 96, 0.1, 1, 0, 1, None) == 3
     assert lib.fa_fwd_split_noalloc(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 4
+    # bf16 only, as fa_fwd_split
+    assert lib.fa_fwd_split_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 2, None) == 3
     # fa_fwd_split still requires its workspace
     assert lib.fa_fwd_split(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 1, 1, 64, 128, 0.1, 1, 0, 1, None) == 1

@@ -1,10 +1,11 @@
-"""GPU parity of split-KV decode attention (fa_fwd_split) and of the merge
-(fa_lse_merge) against the float64 oracle (oracle/decode.py).
+"""GPU parity of split-KV decode attention (fa_fwd_split, fa_fwd_split_fp8)
+and of the merge (fa_lse_merge) against the float64 oracle (oracle/decode.py).
 
-Inputs are the seeded bf16 bytes of ``workloads``.  O is compared element by
-element at the forward's bf16 tolerances (max abs 2e-2, relative L2 5e-3,
-lse 1e-3); the merge alone is compared on partials the oracle made from a
-real key split.
+Inputs are the seeded bf16 or e4m3 bytes of ``workloads`` (the oracle takes
+the dequantised e4m3 values).  O is compared element by element at the
+forward's tolerances (bf16: max abs 2e-2, relative L2 5e-3; fp8: relative L2
+5e-2), lse within 1e-3 for both; the merge alone is compared on partials the
+oracle made from a real key split.
 """
 
 import numpy as np
@@ -69,6 +70,61 @@ def test_split_all_elements(B, H, H_kv, N_q, N_k, d, causal, splits):
     check(errors(o, o_ref, l, l_ref), "bf16", f"split B={B} H={H}/{H_kv} N_q={N_q} N_k={N_k} d={d} S={splits}")
 
 
+def run_split_fp8(x, splits=0, scale=None):
+    import exact_io_aware_48_amd as fa
+    w = x.workload
+    q, k, v = to_device(x)
+    o, lse = fa.fa_fwd_split_fp8(q, k, v, *x.descale, scale=w.softmax_scale if scale is None else scale,
+                                 causal=w.causal, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_fp8(o, l, o_ref, l_ref, what):
+    """fp8: O to the fp8 forward's relative L2 bound (P is rounded to e4m3).  The
+    scores are exact products of the e4m3 values summed in fp32 and the row sums
+    use the unrounded probabilities, so L keeps the bf16 path's bound."""
+    errs = errors(o, o_ref, l, l_ref)
+    check(errs, "fp8", what)
+    assert errs["lse_max"] <= TOL["bf16"]["lse_max"], f"{what}: lse error {errs['lse_max']}"
+
+
+FP8_CASES = [
+    # (B, H, H_kv, N_q, N_k, d, causal, splits): 64-key tiles at every d
+    (2, 8, 2, 1, 1000, 128, True, 0),
+    (1, 32, 8, 1, 4096, 128, False, 0),
+    (1, 4, 1, 3, 777, 64, True, 5),
+    (2, 6, 3, 16, 2048, 64, True, 0),
+    (1, 4, 2, 1, 20, 64, True, 0),            # fewer keys than one tile
+    (1, 16, 2, 8, 500, 128, True, 3),         # 64 rows per K/V head: two row blocks
+    (1, 2, 2, 64, 64, 128, True, 2),          # square: the forward's causal mask; more splits than tiles
+    (2, 8, 2, 1, 1000, 256, True, 0),         # d = 256: 64 KiB ring
+    (1, 16, 2, 8, 3001, 256, True, 3),
+    (1, 4, 4, 1, 20, 256, False, 1),
+    (3, 4, 4, 2, 3000, 64, False, 7),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,N_q,N_k,d,causal,splits", FP8_CASES)
+def test_split_fp8_all_elements(B, H, H_kv, N_q, N_k, d, causal, splits):
+    _print_case("fp8", B, H, H_kv, N_q, N_k, d, causal, splits)
+    w = by_name(BASE).with_(B=B, H=H, H_kv=H_kv, N_q=N_q, N=N_k, d=d, causal=causal, dtype="fp8", seed=200 + N_k)
+    x = make_inputs(w)
+    o, l = run_split_fp8(x, splits)
+    o_ref, l_ref = oracle(x)
+    check_fp8(o, l, o_ref, l_ref, f"split fp8 B={B} H={H}/{H_kv} N_q={N_q} N_k={N_k} d={d} S={splits}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+def test_split_fp8_other_scales(scale):
+    _print_case("fp8 scale", scale)
+    w = by_name(BASE).with_(B=1, H=8, H_kv=2, N_q=4, N=900, d=128, dtype="fp8", seed=6)
+    x = make_inputs(w)
+    o, l = run_split_fp8(x, 0, scale)
+    o_ref, l_ref = oracle(x, scale)
+    check_fp8(o, l, o_ref, l_ref, f"fp8 scale {scale}")
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.7])
 def test_split_other_scales(scale):
     _print_case("scale", scale)
@@ -96,9 +152,12 @@ def test_split_count_changes_only_rounding_and_repeats_bitwise():
 def test_split_full_size_all_elements(w):
     _print_case("full", w.name)
     x = make_inputs(w)
-    o, l = run_split(x)
     o_ref, l_ref = oracle(x)
-    check(errors(o, o_ref, l, l_ref), "bf16", w.name)
+    if w.dtype == "fp8":
+        check_fp8(*run_split_fp8(x), o_ref, l_ref, w.name)
+    else:
+        o, l = run_split(x)
+        check(errors(o, o_ref, l, l_ref), "bf16", w.name)
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])

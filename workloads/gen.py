@@ -93,6 +93,8 @@ WORKLOADS = [
 DECODE_WORKLOADS = [
     Workload("decode_gqa_bf16_b8h32kv8q1n32768d128", 8, 32, 32768, 128, "bf16", True, seed=7, H_kv=8, N_q=1),
     Workload("decode_mha_bf16_b4h32q1n16384d128", 4, 32, 16384, 128, "bf16", True, seed=8, N_q=1),
+    # the first one with an fp8 K/V cache (e4m3 Q, K, V with per-tensor descales)
+    Workload("decode_gqa_fp8_b8h32kv8q1n32768d128", 8, 32, 32768, 128, "fp8", True, seed=7, H_kv=8, N_q=1),
 ]
 
 
