@@ -92,9 +92,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  *                dequantised scores
  *   *_descale  : finite and > 0, else FA_ERR_SCALE
  * Softmax statistics and both products accumulate in float32.  The softmax
- * probabilities are multiplied by 256 and rounded to e4m3 for the P V
- * product; the factor is divided out in float32 and the row sum uses the
- * unrounded probabilities.
+ * probabilities, taken against an exponent base that may trail the row
+ * maximum by up to 2 (log2 units), so at most 2^2, are pre-scaled by 2^6 (at
+ * most 256 then) and rounded to e4m3 for the P V product; the row sum uses
+ * them unrounded, so the factor cancels in O / l, and L removes it.
  */
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8, void* o_bf16, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
