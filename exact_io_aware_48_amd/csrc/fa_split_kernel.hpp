@@ -212,31 +212,70 @@ struct MergeParams {
   int out_bf16;
 };
 
-// One wave per row; lane t handles dims t, t + 64, ...
+// One wave per row.  The splits' L_s are read all at once (lane s holds split
+// s, 64 splits per pass) and reduced across the wave; O column c = lane + 64 j
+// sums exp(L_s - max) O_s over the splits in order, with the O_s loads issued
+// eight at a time (a loop that waited for each load in turn made the merge a
+// chain of 4 S + d/64 * S load latencies).
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+// a butterfly: every lane adds the same two values at every step, so all
+// lanes end with the same sum
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= p.rows) return;
-  float m = -INFINITY;
-  for (int s = 0; s < p.S; ++s) m = fmaxf(m, p.lse_part[(int64_t)s * p.rows + row]);
+  if (row >= p.rows) return;                       // the whole wave: one row per wave
+  const int S = p.S;
+  auto lse_of = [&](int s) __attribute__((always_inline)) { return p.lse_part[(int64_t)s * p.rows + row]; };
+  const float l_lane = lane < S ? lse_of(lane) : -INFINITY;   // splits 0..63, kept
+  float m = l_lane;
+  for (int s0 = 64; s0 < S; s0 += 64) m = fmaxf(m, s0 + lane < S ? lse_of(s0 + lane) : -INFINITY);
+  m = wave_max64(m);
   const float m_use = m == -INFINITY ? 0.f : m;
-  float tot = 0.f;
-  for (int s = 0; s < p.S; ++s) tot += __expf(p.lse_part[(int64_t)s * p.rows + row] - m_use);
+  const float w_lane = __expf(l_lane - m_use);                 // the weight of split `lane` (0 past S)
+  float part = w_lane;
+  for (int s0 = 64; s0 < S; s0 += 64) part += s0 + lane < S ? __expf(lse_of(s0 + lane) - m_use) : 0.f;
+  const float tot = wave_sum64(part);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   if (lane == 0) p.lse[row] = tot > 0.f ? m_use + __logf(tot) : -INFINITY;
-  for (int c = lane; c < p.d; c += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < p.S; ++s) {
-      const float w = __expf(p.lse_part[(int64_t)s * p.rows + row] - m_use);
-      acc = __builtin_fmaf(w, p.o_part[((int64_t)s * p.rows + row) * p.d + c], acc);
+  const int64_t stride = (int64_t)p.rows * p.d;   // between splits
+  auto columns = [&](auto weight) __attribute__((always_inline)) {
+    for (int c = lane; c < p.d; c += 64) {
+      const float* src = p.o_part + row * p.d + c;
+      float acc = 0.f;
+      int s = 0;
+      for (; s + 8 <= S; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(s + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc = __builtin_fmaf(weight(s + u), v[u], acc);
+      }
+      for (; s < S; ++s) acc = __builtin_fmaf(weight(s), src[s * stride], acc);
+      const float x = acc * inv;
+      if (p.out_bf16) {
+        static_cast<uint16_t*>(p.o)[row * p.d + c] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+      } else {
+        static_cast<float*>(p.o)[row * p.d + c] = x;
+      }
     }
-    const float x = acc * inv;
-    if (p.out_bf16) {
-      static_cast<uint16_t*>(p.o)[row * p.d + c] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
-    } else {
-      static_cast<float*>(p.o)[row * p.d + c] = x;
-    }
-  }
+  };
+  // the weight of split s: lane s's w_lane (at most 64 splits), else formed again
+  if (S <= 64)
+    columns([&](int s) __attribute__((always_inline)) {
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), s));
+    });
+  else
+    columns([&](int s) __attribute__((always_inline)) { return __expf(lse_of(s) - m_use); });
 }
 
 }  // namespace fa

@@ -57,6 +57,7 @@ CASES = [
     (1, 16, 2, 8, 3001, 256, True, 3),
     (1, 4, 4, 1, 20, 256, False, 1),
     (2, 4, 1, 5, 2048, 256, False, 0),
+    (1, 4, 2, 1, 4000, 128, True, 100),       # more than 64 splits: the merge forms the weights again
 ]
 
 
@@ -185,3 +186,28 @@ def test_merge_entry_point(out_dtype):
                              out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert np.isneginf(l2.cpu().numpy()[3]) and np.all(o2.cpu().numpy()[3] == 0)
+
+
+@pytest.mark.parametrize("num_parts,d", [(13, 200), (70, 64), (130, 40)])
+def test_merge_many_parts(num_parts, d):
+    """Part counts off the merge's batches of eight and past 64 (weights formed
+    again from L_s), head dims off its 64-column steps, rows off its four per
+    block, and an empty part; fp32 output against the float64 merge."""
+    import exact_io_aware_48_amd as fa
+    _print_case("merge many", num_parts, d)
+    rng = np.random.default_rng(num_parts)
+    rows, N_k = 37, 10 * num_parts
+    q, k, v = rng.standard_normal((rows, d)), rng.standard_normal((N_k, d)), rng.standard_normal((N_k, d))
+    cuts = np.linspace(0, N_k, num_parts + 1).astype(int)
+    cuts[3] = cuts[2]                                  # part 2 is empty
+    parts = [partial_over_keys(q, k, v, 0.1, False, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    o_parts = np.stack([p[0] for p in parts]).astype(np.float32)
+    l_parts = np.stack([p[1] for p in parts]).astype(np.float32)
+    o_ref, l_ref = merge_partials(o_parts.astype(np.float64), l_parts.astype(np.float64))
+    o, l = fa.fa_lse_merge(torch.from_numpy(o_parts).cuda(), torch.from_numpy(l_parts).cuda(),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy().astype(np.float64)
+    l = l.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(o - o_ref)) <= 1e-5 * max(1.0, np.max(np.abs(o_ref)))
+    assert np.max(np.abs(l - l_ref)) <= 1e-5 * max(1.0, np.max(np.abs(l_ref)))
