@@ -55,6 +55,7 @@ levels from the amdgpu kernel driver's sysfs files right after the headline's ti
     python bench.py --summarize-counters DIR... --workload NAME
                                                write profiles/counters_<NAME>.txt from SQ counter passes
     python bench.py --timeline NAME...         per-workgroup phase timeline of one launch (diagnostic build)
+    python bench.py --issue-probes             MFMA / FMA / exp / LDS-read issue microbenchmarks (probe library)
 """
 
 import argparse
@@ -636,6 +637,61 @@ def roofline_block(w, t):
     return blk
 
 
+# ------------------------------------------------------------------ issue probes
+ROLE_PROBES = [(1, "MFMA waves only (8 MFMA per iteration)"), (2, "FMA waves only (64 FMA per iteration)"),
+               (3, "MFMA waves + FMA waves"), (6, "exp waves only (64 exp per iteration)"),
+               (7, "MFMA waves + exp waves")]
+
+
+def issue_probes(iters=2000, reps=40, settle_launches=400):
+    """Run the issue-rate microbenchmarks of libfa_probe.so (csrc/fa_issue_probe.hip)
+    and return their table as text lines: per configuration the launch time, the
+    time per wave-iteration, for mixed work the sum of its parts timed alone at
+    the same waves per SIMD, and the sclk level right after it.  A settling run
+    (about 0.2 s of the MFMA + exp mix) comes first, so that the first rows do
+    not meet a clock still ramping up from idle."""
+    import ctypes
+    import torch
+    from exact_io_aware_48_amd import _lib
+    lib = _lib.load_probe()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    ms = ctypes.c_float()
+
+    def run(fn, i):
+        st = fn(i, out.data_ptr(), out.numel(), iters, reps, ctypes.byref(ms))
+        if st != 0:
+            raise RuntimeError(f"probe {i}: status {st}")
+        return ms.value
+
+    if lib.fa_probe_mixed(4, out.data_ptr(), out.numel(), iters, settle_launches, ctypes.byref(ms)) != 0:
+        raise RuntimeError("probe settling run failed")
+
+    def sclk():
+        c = read_clocks(("sclk",))
+        return ", ".join(f"{v}" for v in c.values()) if isinstance(c, dict) else "?"
+
+    rows, alone = [], {}
+    for i in range(lib.fa_probe_mixed_count()):
+        wk = (ctypes.c_int * 5)()
+        lib.fa_probe_mixed_work(i, wk)
+        wps, mf, fma, ex, lds = list(wk)
+        t = run(lib.fa_probe_mixed, i)
+        if (mf > 0) + (fma > 0) + (ex > 0) + (lds > 0) == 1:
+            alone[(wps, mf, fma, ex, lds)] = t
+        # mixed work without LDS reads: the sum of its MFMA, FMA and exp parts where each was timed alone
+        parts = [alone.get(key) for n, key in ((mf, (wps, mf, 0, 0, 0)), (fma, (wps, 0, fma, 0, 0)),
+                                               (ex, (wps, 0, 0, ex, 0))) if n]
+        summed = len(parts) > 1 and lds == 0 and None not in parts
+        rows.append(f"{lib.fa_probe_mixed_name(i).decode():58s} {t:8.3f} ms  {t * 1e6 / iters:7.1f} ns/iter"
+                    + f"  sclk {sclk():>8s}" + (f"  parts alone {sum(parts):.3f} ms" if summed else ""))
+    for role, name in ROLE_PROBES:
+        t = run(lib.fa_probe_roles, role)
+        rows.append(f"{'split roles: ' + name:58s} {t:8.3f} ms  {t * 1e6 / iters:7.1f} ns/iter  sclk {sclk():>8s}")
+    return [f"issue probes: {cus} workgroups (one per CU), {iters} iterations, mean of {reps} launches after "
+            f"{reps // 2 + 1} warm-up launches, following a {settle_launches}-launch settling run", ""] + rows
+
+
 # ------------------------------------------------------------------ timeline
 def timeline_summary(w, lib, launches=200):
     """Per-workgroup phases of one forward launch on workload w, from the
@@ -736,6 +792,9 @@ def main():
     ap.add_argument("--timeline", nargs="+", metavar="NAME",
                     help="per-workgroup phase timeline of one forward launch of each workload, from the "
                          "diagnostic build (python -m exact_io_aware_48_amd.build --timeline); one JSON line each")
+    ap.add_argument("--issue-probes", action="store_true",
+                    help="the issue-rate microbenchmarks (python -m exact_io_aware_48_amd.build --probes): MFMA, "
+                         "FMA, exp and LDS reads in one wave or in different waves; writes profiles/issue_probes.txt")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -761,6 +820,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    if args.issue_probes:
+        lines = issue_probes()
+        lines.insert(1, "command: python bench.py --issue-probes")
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(os.path.join(PROFILES, "issue_probes.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines), flush=True)
+        return 0
     if args.timeline:
         from exact_io_aware_48_amd import _lib
         tl = _lib.load_timeline()

@@ -31,6 +31,28 @@ def load_timeline():
     return _declare(ctypes.CDLL(path))
 
 
+def load_probe():
+    """The issue-rate microbenchmarks (libfa_probe.so, a diagnostic library of
+    their own, csrc/fa_issue_probe.hip); raise if they have not been built."""
+    path = os.path.join(os.path.dirname(LIB_PATH), "libfa_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_io_aware_48_amd.build --probes`")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    pf = ctypes.POINTER(ctypes.c_float)
+    lib.fa_probe_mixed_count.argtypes = []
+    lib.fa_probe_mixed_count.restype = i32
+    lib.fa_probe_mixed_name.argtypes = [i32]
+    lib.fa_probe_mixed_name.restype = ctypes.c_char_p
+    lib.fa_probe_mixed_work.argtypes = [i32, ctypes.POINTER(i32)]
+    lib.fa_probe_mixed_work.restype = i32
+    lib.fa_probe_mixed.argtypes = [i32, vp, i64, i32, i32, pf]
+    lib.fa_probe_mixed.restype = i32
+    lib.fa_probe_roles.argtypes = [i32, vp, i64, i32, i32, pf]
+    lib.fa_probe_roles.restype = i32
+    return lib
+
+
 def _declare(lib):
     vp, i64, f32, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i32, vp]

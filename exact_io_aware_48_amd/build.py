@@ -1,11 +1,13 @@
-"""Build step: compile the HIP sources into the in-tree shared library.
+"""Build step: compile the HIP sources into the in-tree shared libraries.
 
-    python -m exact_io_aware_48_amd.build [--timeline]
+    python -m exact_io_aware_48_amd.build [--timeline | --probes | --all]
 
 produces ``exact_io_aware_48_amd/libfa_fwd.so`` for gfx950 (``--timeline``:
 the diagnostic build ``libfa_fwd_timeline.so``, whose forward kernels stamp
-their phases; see fa_timeline_read).  It always recompiles (a build check
-must not trust a stale binary).
+their phases, see fa_timeline_read; ``--probes``: ``libfa_probe.so``, the
+issue-rate microbenchmarks of ``csrc/fa_issue_probe.hip`` that
+``bench.py --issue-probes`` runs; ``--all``: the three).  It always
+recompiles (a build check must not trust a stale binary).
 """
 
 import os
@@ -21,6 +23,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa_fwd.so")
 # diagnostic build with per-workgroup timeline stamps (-DFA_TIMELINE)
 LIB_TIMELINE = os.path.join(PKG, "libfa_fwd_timeline.so")
+# diagnostic microbenchmarks (not part of the product library)
+LIB_PROBE = os.path.join(PKG, "libfa_probe.so")
+PROBE_SOURCE = os.path.join(CSRC, "fa_issue_probe.hip")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, f) for f in ("fa_api.hip", "fa_var_api.hip", "fa_bwd_api.hip", "fa_split_api.hip")]
@@ -78,5 +83,32 @@ def build(verbose=False, jobs=None, timeline=False):
     return out
 
 
+def build_probes(verbose=False):
+    """Compile the issue-rate microbenchmarks into their own library."""
+    tmpdir = tempfile.mkdtemp(prefix="fa_build_")
+    try:
+        obj = os.path.join(tmpdir, "fa_issue_probe.o")
+        _run(compile_cmd(PROBE_SOURCE, obj))
+        tmp = LIB_PROBE + ".tmp"
+        _run(link_cmd([obj], tmp))
+        os.replace(tmp, LIB_PROBE)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
+    if verbose:
+        print(f"built {LIB_PROBE}")
+    return LIB_PROBE
+
+
+def build_all(verbose=False):
+    """The product library, its timeline build and the probe library."""
+    return [build(verbose), build(verbose, timeline=True), build_probes(verbose)]
+
+
 if __name__ == "__main__":
-    build(verbose=True, timeline="--timeline" in sys.argv[1:])
+    args = sys.argv[1:]
+    if "--all" in args:
+        build_all(verbose=True)
+    elif "--probes" in args:
+        build_probes(verbose=True)
+    else:
+        build(verbose=True, timeline="--timeline" in args)

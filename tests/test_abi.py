@@ -43,6 +43,33 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(raw, name), name
 
 
+PROBE = os.path.join(ROOT, "exact_io_aware_48_amd", "libfa_probe.so")
+
+
+@pytest.mark.skipif(not os.path.exists(PROBE), reason="probe library not built")
+def test_probe_library_host_side():
+    """The probe library's table and argument checks (no launch: a NULL output
+    buffer or a zero iteration count is refused before any HIP call)."""
+    from exact_io_aware_48_amd import _lib
+    lib = _lib.load_probe()
+    n = lib.fa_probe_mixed_count()
+    assert n == 12
+    names = [lib.fa_probe_mixed_name(i).decode() for i in range(n)]
+    assert len(set(names)) == n and lib.fa_probe_mixed_name(n) == b""
+    w = (ctypes.c_int * 5)()
+    for i in range(n):
+        assert lib.fa_probe_mixed_work(i, w) == 0
+        wps, mf, fma, ex, lds = list(w)
+        assert wps in (1, 2) and names[i].startswith(f"{wps} wave")
+        assert (f"{mf} MFMA" in names[i]) == (mf > 0) and (f"{fma} FMA" in names[i]) == (fma > 0)
+        assert (f"{ex} exp" in names[i]) == (ex > 0) and (f"{lds} ds_read" in names[i]) == (lds > 0)
+    assert lib.fa_probe_mixed_work(n, w) == 2 and lib.fa_probe_mixed_work(-1, w) == 2
+    ms = ctypes.c_float()
+    assert lib.fa_probe_mixed(0, None, 1 << 20, 10, 1, ctypes.byref(ms)) == 2
+    assert lib.fa_probe_roles(1, None, 1 << 20, 10, 1, ctypes.byref(ms)) == 2
+    assert lib.fa_probe_mixed(0, FAKE, 1 << 20, 0, 1, ctypes.byref(ms)) == 2
+
+
 def test_timeline_read_is_unsupported_in_the_product_build(lib):
     import numpy as np
     buf = np.zeros(12, dtype=np.uint64)
