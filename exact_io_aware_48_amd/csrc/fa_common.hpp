@@ -169,10 +169,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, const char FA_LDS* lds) 
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0v) : "memory");
 }
 // The same load addressed as a wave-uniform 64-bit base (SGPRs) plus a
-// per-lane 32-bit byte offset.
+// per-lane 32-bit byte offset.  NT: with the non-temporal (streaming) cache
+// hint, for data each workgroup reads once and no other one reads again
+// (split-KV decoding's K/V stream: 11-15% faster on MI355X).  Kernels whose
+// workgroups share K/V through the L2 keep it off (it cost them 4-16%).
+template <bool NT = false>
 __device__ __forceinline__ void dma16_s(const char* sbase, int voff, const char FA_LDS* lds) {
   const uint32_t m0v = (uint32_t)(uintptr_t)lds;
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+  if constexpr (NT)
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0v) : "memory");
 }
 // Wait until at most N of this wave's vector-memory loads are outstanding
 // (they complete in issue order, so the older ones are then done).

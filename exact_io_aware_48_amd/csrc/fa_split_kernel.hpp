@@ -119,8 +119,9 @@ __global__ __launch_bounds__(NW * 64) void fa_split_kernel(SplitParams p) {
   const int j0 = k_lo / BC, j1 = (k_hi + BC - 1) / BC;
   const int first_row_last = CAUSAL ? N_k - p.N_q : N_k - 1;   // the smallest limit of any row
 
-  Stager<D, BC, NW, MODE, false> kstage;
-  Stager<D, BC, NW, MODE, true> vstage;
+  // each K/V byte is read by this workgroup alone: streaming loads
+  Stager<D, BC, NW, MODE, false, true> kstage;
+  Stager<D, BC, NW, MODE, true, true> vstage;
   kstage.init(wave, lane);
   vstage.init(wave, lane);
   const char* kglob = static_cast<const char*>(p.k) + kv_off * G::EB;

@@ -612,8 +612,9 @@ struct Tile {
 // fetches.  The per-lane byte offsets inside a full tile do not depend on the
 // tile, so they are computed once; the tile's base address is wave-uniform
 // and travels in SGPRs.  Rows past the end of the sequence re-read row N-1:
-// their scores are masked, so they only ever meet P = 0.
-template <int D, int BC, int NW, int MODE, bool IS_V>
+// their scores are masked, so they only ever meet P = 0.  NT: streaming
+// loads (dma16_s), for a K/V stream no other workgroup reads.
+template <int D, int BC, int NW, int MODE, bool IS_V, bool NT = false>
 struct Stager {
   using G = Geo<D, BC, NW, MODE>;
   // Chunk i of a thread lies NW * 1024 bytes (ADV rows) after chunk 0.  When
@@ -649,17 +650,17 @@ struct Stager {
     if (row0 + BC <= N) {
 #pragma unroll
       for (int i = 0; i < G::UPT; ++i)
-        dma16_s(base, AFFINE ? ofs[0] + i * NW * 1024 : ofs[i], dst + (i * NW + wave) * 1024);
+        dma16_s<NT>(base, AFFINE ? ofs[0] + i * NW * 1024 : ofs[i], dst + (i * NW + wave) * 1024);
     } else {
       const int last = N - 1 - row0;
 #pragma unroll
       for (int i = 0; i < G::UPT; ++i) {
         if constexpr (AFFINE) {
-          dma16_s(base, min(row0_ + i * ADV, last) * G::ROWB + swz0_, dst + (i * NW + wave) * 1024);
+          dma16_s<NT>(base, min(row0_ + i * ADV, last) * G::ROWB + swz0_, dst + (i * NW + wave) * 1024);
         } else {
           const int off = (i * NW + wave) * 1024 + lane * 16;
           const int row = off / G::ROWB, pc = (off % G::ROWB) >> 4;
-          dma16_s(base, min(row, last) * G::ROWB + ((pc ^ swz(row)) << 4), dst + (i * NW + wave) * 1024);
+          dma16_s<NT>(base, min(row, last) * G::ROWB + ((pc ^ swz(row)) << 4), dst + (i * NW + wave) * 1024);
         }
       }
     }
