@@ -121,9 +121,10 @@ fa_status make_plan(int64_t B, int64_t H, int64_t H_kv, int64_t N_q, int64_t N_k
   return FA_OK;
 }
 
-// K/V ring depth.  Measured on MI355X at 2 to 5 stages: decode streams at
-// 5.5-5.8 TB/s whatever the depth (a 1 GiB device copy reaches 5.2), so the
-// plain double buffer is kept.
+// K/V ring depth.  Measured on MI355X at 2 to 5 stages with plain loads:
+// 5.5-5.8 TB/s whatever the depth (a 1 GiB device copy reaches 5.2).  With
+// the streaming loads a third stage is slower (GQA decode 155.8 -> 162.6 us,
+// fp8 80.9 -> 83.5 us), so the plain double buffer is kept.
 constexpr int kSplitNS = 2;
 
 template <int D, bool CAUSAL, int MODE>
