@@ -450,19 +450,40 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     dk_base = p.part_out + hp * slab;
     dv_base = p.part_out + (p.parts + hp) * slab;
   }
+  // dK^T and dV^T leave through LDS as whole fp32 rows (one tensor per
+  // pass): each wave writes its KW rows into its own region of the Q/dO ring
+  // and V area, free since the last barrier, and reads them back a full row
+  // segment per lane group, so every store instruction covers whole rows.
+  // The 16-byte chunk of a row is XORed with row % 16, so that the 16 rows a
+  // write instruction touches at one logical chunk fall in distinct banks.
+  // (Stored from the accumulator layout, 16 rows x 64 bytes per instruction,
+  // these stores bounded GPT-2-small's backward at 5.1 of 67.5 us.)
+  constexpr int OROWB = 4 * D, OCPR = OROWB / 16;   // fp32 row bytes, chunks per row
+  constexpr int WREG = KW * OROWB;                   // one wave's rows of one tensor
+  constexpr int RPI = 1024 / OROWB;                  // rows per wave instruction
+  static_assert(NW * WREG <= (int)sizeof(smem_raw) && OCPR >= 16 && KW % RPI == 0, "dK/dV staging fits");
+  char FA_LDS* const wreg = smem + wave * WREG;
+  auto stage_out = [&](const f32x4 (&acc)[KBW][NDB], float mul, float* base) __attribute__((always_inline)) {
 #pragma unroll
-  for (int kb = 0; kb < KBW; ++kb) {
-    const int key = kw0 + 16 * kb + m;
-    if (key < N) {
-      float* dkp = dk_base + kv_off + (int64_t)key * D + 4 * g;
-      float* dvp = dv_base + kv_off + (int64_t)key * D + 4 * g;
+    for (int kb = 0; kb < KBW; ++kb)
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        *reinterpret_cast<f32x4*>(dkp + 16 * db) = dk[kb][db] * sc;
-        *reinterpret_cast<f32x4*>(dvp + 16 * db) = dv[kb][db];
+        const int row = 16 * kb + m;                  // dims 16 db + 4 g .. + 3 of key kw0 + row
+        *reinterpret_cast<f32x4 FA_LDS*>(wreg + row * OROWB + (((4 * db + g) ^ (row & 15)) << 4)) = acc[kb][db] * mul;
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the reads below fetch other lanes' writes
+    const int rr = lane / OCPR, lc = lane % OCPR;
+#pragma unroll
+    for (int i = 0; i < KW / RPI; ++i) {
+      const int row = i * RPI + rr;
+      const f32x4 v = *reinterpret_cast<const f32x4 FA_LDS*>(wreg + row * OROWB + ((lc ^ (row & 15)) << 4));
+      if (kw0 + row < N)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(base + kv_off + (int64_t)(kw0 + row) * D + 4 * lc));
     }
-  }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read out before the next tensor's writes
+  };
+  stage_out(dk, sc, dk_base);
+  stage_out(dv, 1.f, dv_base);
 }
 
 // dk = sum of the parts' dK, dv likewise (four floats per thread)
@@ -618,17 +639,39 @@ void fa_bwd_dq_kernel(BwdParams p) {
   }
   if (j < n_tiles) step(j, 0);
 
-  if (my_q < N) {
-    float* dst = p.dq + head_off + (int64_t)my_q * D;
-    const float sc = p.scale;
+  // dQ leaves through LDS as whole row segments, as dK and dV do in their
+  // kernel: the K/V ring (free since the last barrier) holds NW x 32 rows of
+  // D / NPASS dims per pass, chunk XOR (row % 16) against bank conflicts,
+  // and the stores are non-temporal (dQ is not read again here).
+  constexpr int NPASS = NW * 32 * 4 * D <= 2 * STAGEB ? 1 : NW * 32 * 4 * D <= 4 * STAGEB ? 2 : 4;
+  constexpr int RB = 4 * D / NPASS, CPRR = RB / 16;   // region row bytes, 16-byte chunks per region row
+  constexpr int DBP = NDB / NPASS;                    // 32-wide d-blocks per pass
+  constexpr int RPI = 1024 / RB;                      // rows per wave instruction
+  static_assert(NW * 32 * RB <= 2 * STAGEB && CPRR >= 16 && NDB % NPASS == 0, "dQ staging fits");
+  char FA_LDS* const wreg = smem + wave * 32 * RB;
+  const float sc = p.scale;
+  const int rr = lane / CPRR, lc = lane % CPRR;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int pass = 0; pass < NPASS; ++pass) {
+    // lane (n, hf): dims 32 db + 8 g + 4 hf .. + 3 of query row n
+#pragma unroll
+    for (int b = 0; b < DBP; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = 32 * db + 8 * g + 4 * ln.hf;
-        *reinterpret_cast<f32x4*>(dst + col) =
+        const int db = DBP * pass + b, c = 8 * b + 2 * g + ln.hf;
+        *reinterpret_cast<f32x4 FA_LDS*>(wreg + ln.n * RB + ((c ^ (ln.n & 15)) << 4)) =
             f32x4{dq[db][4 * g] * sc, dq[db][4 * g + 1] * sc, dq[db][4 * g + 2] * sc, dq[db][4 * g + 3] * sc};
       }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the reads below fetch other lanes' writes
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + rr;
+      const f32x4 v = *reinterpret_cast<const f32x4 FA_LDS*>(wreg + row * RB + ((lc ^ (row & 15)) << 4));
+      if (qw0 + row < N)
+        __builtin_nontemporal_store(
+            v, reinterpret_cast<f32x4*>(p.dq + head_off + (int64_t)(qw0 + row) * D + pass * (D / NPASS) + 4 * lc));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read out before the next pass's writes
   }
 }
 
