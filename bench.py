@@ -547,7 +547,8 @@ def summarize_counters(dirs, workload_name, command=""):
         raise SystemExit(f"no forward-kernel dispatch in {dirs}")
     mean = {k: sum(v) / len(v) for k, v in sorted(vals.items())}
     lines = [f"# SQ counters of the forward kernel: {workload_name}", "",
-             f"command (one pass per counter set): {command}", "",
+             f"command (one pass per counter set): {command}",
+             f"kernel sources sha: {kernel_source_hash()}", "",
              "counter                          dispatches   mean per dispatch"]
     lines += [f"{k:32s} {len(vals[k]):10d}   {mean[k]:18.1f}" for k in mean]
     mf = mean.get("SQ_INSTS_MFMA")
@@ -764,6 +765,37 @@ def timeline_summary(w, lib, launches=200):
     }
 
 
+
+def summarize_timelines(path, command="", out=None):
+    """Write profiles/timeline_forward_workloads.txt from the JSON lines of
+    ``bench.py --timeline`` (one per workload)."""
+    lines = ["Per-workgroup timelines of one forward launch per workload (diagnostic build, "
+             "s_memrealtime at 100 MHz; microseconds)",
+             f"command: {command}", f"kernel sources sha: {kernel_source_hash()}",
+             "phases per workgroup: start offset (dispatch), prologue (Q and first K/V tiles), main loop, "
+             "O store (incl. a workgroup barrier); percentiles p0 p10 p50 p90 p100"]
+    with open(path) as f:
+        recs = [json.loads(ln) for ln in f if ln.startswith("{")]
+    if not recs:
+        raise SystemExit(f"no timeline record in {path}")
+    for r in recs:
+        wpc = {str(k): v for k, v in r["workgroups_per_cu"].items()}
+        lines += ["", f"== {r['workload']}: {r['workgroups']} workgroups on {r['cus']} CUs {wpc}, span {r['span_us']}"]
+        for k in ("start_offset", "prologue", "main_loop", "o_store", "end", "loop_sum_per_cu", "last_end_per_cu"):
+            lines.append(f"  {k:34s} {r[k]}")
+        gap = r.get("gap_between_sequential_workgroups_on_a_cu")
+        lines.append("  gap_between_sequential_workgroups_on_a_cu "
+                     + (str(gap) if gap else "  (none: the CU's workgroups ran side by side)"))
+        lines.append("  by start rank on a CU: " + ", ".join(
+            f"{k}: loop {v['main_loop_p50']} end {v['end_p50']}" for k, v in r["by_start_rank_on_cu"].items()))
+        lines.append("  per XCD (loop sum per CU mean / last end): " + ", ".join(
+            f"{k}: {v['loop_sum_per_cu_mean']}/{v['last_end']}" for k, v in r["xcd"].items()))
+    out = out or os.path.join(PROFILES, "timeline_forward_workloads.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -787,6 +819,8 @@ def main():
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_DIR",
                     help="write profiles/counters_<NAME>.txt from rocprofv3 --pmc passes over --workload")
+    ap.add_argument("--summarize-timelines", metavar="JSONL",
+                    help="write profiles/timeline_forward_workloads.txt from the output of --timeline")
     ap.add_argument("--command", default="", help="the profiling command, recorded in the summary")
     ap.add_argument("--summary-prefix", default="kernel_trace", help="file name prefix of --summarize-trace")
     ap.add_argument("--timeline", nargs="+", metavar="NAME",
@@ -799,6 +833,9 @@ def main():
 
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command)
+        return 0
+    if args.summarize_timelines:
+        summarize_timelines(args.summarize_timelines, args.command)
         return 0
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload, args.command)

@@ -146,3 +146,37 @@ def test_summaries_recognise_both_forward_kernels():
     assert bench.is_forward_kernel("void fa::fa_fwd_pipe_kernel<128, 64, 8, true>(fa::Params)")
     assert not bench.is_forward_kernel("void fa::fa_bwd_dq_kernel<128, 8, true>(fa::BwdParams)")
     assert not bench.is_forward_kernel("__amd_rocclr_copyBuffer")
+
+
+def test_summarize_timelines_writes_each_workload(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    pct = [0.0, 1.0, 2.0, 3.0, 4.0]
+    rec = {"workload": "gpt2s_causal_bf16_b8h12n1024d64", "workgroups": 768, "span_us": 22.5, "cus": 256,
+           "workgroups_per_cu": {"3": 256}, "start_offset": pct, "prologue": pct, "main_loop": pct, "o_store": pct,
+           "end": pct, "loop_sum_per_cu": pct, "last_end_per_cu": pct,
+           "gap_between_sequential_workgroups_on_a_cu": None,
+           "by_start_rank_on_cu": {"0": {"main_loop_p50": 17.5, "end_p50": 20.5}},
+           "xcd": {"0": {"loop_sum_per_cu_mean": 43.8, "last_end": 22.1}}}
+    src = tmp_path / "t.jsonl"
+    src.write_text("noise\n" + json.dumps(rec) + "\n" + json.dumps(dict(rec, workload="bertl_bf16_b16h16n512d64",
+                   gap_between_sequential_workgroups_on_a_cu=[0.2, 0.3, 0.4, 0.5, 0.6])) + "\n")
+    bench.summarize_timelines(str(src), "cmd here")
+    text = (tmp_path / "timeline_forward_workloads.txt").read_text()
+    assert "command: cmd here" in text and f"kernel sources sha: {bench.kernel_source_hash()}" in text
+    assert "== gpt2s_causal_bf16_b8h12n1024d64: 768 workgroups on 256 CUs {'3': 256}, span 22.5" in text
+    assert "== bertl_bf16_b16h16n512d64" in text and "[0.2, 0.3, 0.4, 0.5, 0.6]" in text
+    assert "ran side by side" in text and "0: loop 17.5 end 20.5" in text and "0: 43.8/22.1" in text
+
+
+def test_counter_summary_records_the_source_hash(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    d = tmp_path / "sq"
+    d.mkdir()
+    (d / "sq_counter_collection.csv").write_text(
+        "Kernel_Name,Counter_Name,Counter_Value\n"
+        "\"fa::fa_fwd_kernel<64, 64, 4, 0, true, false, 0, false, 0>(fa::Params)\",SQ_INSTS_MFMA,100\n"
+        "\"fa::fa_fwd_kernel<64, 64, 4, 0, true, false, 0, false, 0>(fa::Params)\",SQ_INSTS_VALU,1200\n")
+    bench.summarize_counters([str(d)], "gpt2s_causal_bf16_b8h12n1024d64", "cmd")
+    text = (tmp_path / "counters_gpt2s_causal_bf16_b8h12n1024d64.txt").read_text()
+    assert f"kernel sources sha: {bench.kernel_source_hash()}" in text
+    assert "VALU instructions per MFMA (the count includes the MFMAs): 12.00" in text
