@@ -748,8 +748,12 @@ def timeline_summary(w, lib, launches=200):
     xcds = {}
     for xc in sorted(set(xcc.tolist())):
         keys = [k for k in cus if k[0] == xc]
+        ids = np.array([i for k in keys for i in cus[k]])
         xcds[int(xc)] = {"loop_sum_per_cu_mean": round(float(np.mean([loop[cus[k]].sum() for k in keys])), 2),
-                         "last_end": round(float(max(en[cus[k]].max() for k in keys)), 2)}
+                         "last_end": round(float(max(en[cus[k]].max() for k in keys)), 2),
+                         # main-loop median by start rank: whether an XCD's pace changes once others finish
+                         "loop_p50_by_rank": [round(float(np.median(loop[ids[rank[ids] == r]])), 2)
+                                              for r in range(rank[ids].max() + 1)]}
     return {
         "workload": w.name, "workgroups": int(nwg), "span_us": round(float(en.max()), 2),
         "percentiles": "p0 p10 p50 p90 p100",
@@ -790,6 +794,9 @@ def summarize_timelines(path, command="", out=None):
             f"{k}: loop {v['main_loop_p50']} end {v['end_p50']}" for k, v in r["by_start_rank_on_cu"].items()))
         lines.append("  per XCD (loop sum per CU mean / last end): " + ", ".join(
             f"{k}: {v['loop_sum_per_cu_mean']}/{v['last_end']}" for k, v in r["xcd"].items()))
+        if all("loop_p50_by_rank" in v for v in r["xcd"].values()):
+            lines.append("  per XCD main loop p50 by start rank on a CU: " + ", ".join(
+                f"{k}: {v['loop_p50_by_rank']}" for k, v in r["xcd"].items()))
     out = out or os.path.join(PROFILES, "timeline_forward_workloads.txt")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
