@@ -68,6 +68,8 @@ struct Tile {
     int v_row, v_col;           // per-lane parts of the V^T transpose-read address
     int ka[PIPE_ADDR ? 8 : 1];  // bf16: K-read offsets of d-steps c < 8 (step c + 8: +256 bytes)
     int va[PIPE_ADDR ? 4 : 1];  // bf16: V^T-read offsets of d-blocks db < 4 (db + 4: +256 bytes)
+    int kf[MODE == MODE_FP8 ? 2 * QK_STEPS : 1];  // fp8: K-read offsets of d-step c, halves 0 and 1
+    int vf[MODE == MODE_FP8 ? NDB : 1];           // fp8: V^T-read offsets of d-block db
   };
 
   static __device__ __forceinline__ Lane lane_info(int lane) {
@@ -82,6 +84,26 @@ struct Tile {
     } else {
       ln.v_row = 4 * ln.hf + ((lane >> 2) & 3);
       ln.v_col = 2 * (16 * (grp & 1) + 4 * (lane & 3));
+    }
+    if constexpr (MODE == MODE_FP8) {
+      // Whole per-lane offsets, formed once: K row n (+ 32 kb), chunk
+      // (4c + 2hf + j) ^ swz_k(n) in kf[2c + j]; V^T rows v_row (+ 16 t + 64 s), byte
+      // column 32 db + v_col.  Both swizzles repeat every 16 rows, so the
+      // row steps are instruction immediates.  The empty asm hides how an
+      // offset was formed: otherwise the compiler keeps the row and column
+      // parts apart and adds them again before every read (12 VALU
+      // instructions per tile at d = 256).
+#pragma unroll
+      for (int i = 0; i < 2 * QK_STEPS; ++i) {
+        ln.kf[i] = ln.n * G::ROWB + (((4 * (i >> 1) + 2 * ln.hf + (i & 1)) ^ swz_k<G::CPR>(ln.n)) << 4);
+        asm volatile("" : "+v"(ln.kf[i]));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + ln.v_col;
+        ln.vf[db] = ln.v_row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(ln.v_row)) << 4) | (col & 15));
+        asm volatile("" : "+v"(ln.vf[db]));
+      }
     }
     if constexpr (PIPE_ADDR) {
       // K row n (+ 32 kb), chunk (2c + hf) ^ (n % 16): the swizzle leaves bit 4
@@ -265,14 +287,13 @@ struct Tile {
   using Op = typename std::conditional<MODE == MODE_FP8, i32x8, bf16x8>::type;
 
   static __device__ __forceinline__ Op k_operand(const char FA_LDS* kbase, int c, int kb, const Lane& ln) {
-    const int row = 32 * kb + ln.n;
     if constexpr (MODE == MODE_FP8) {
-      const int sw = swz_k<G::CPR>(row);
-      const char FA_LDS* rp = kbase + row * G::ROWB;
-      i32x4 a0 = lds_read16(rp + (((4 * c + 2 * ln.hf) ^ sw) << 4));
-      i32x4 a1 = lds_read16(rp + (((4 * c + 2 * ln.hf + 1) ^ sw) << 4));
+      const char FA_LDS* rp = kbase + 32 * kb * G::ROWB;
+      i32x4 a0 = lds_read16(rp + ln.kf[2 * c]);
+      i32x4 a1 = lds_read16(rp + ln.kf[2 * c + 1]);
       return i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     } else {
+      const int row = 32 * kb + ln.n;
       return __builtin_bit_cast(bf16x8, lds_read16(kbase + row * G::ROWB + (((2 * c + ln.hf) ^ swz_k<G::CPR>(row)) << 4)));
     }
   }
@@ -285,10 +306,7 @@ struct Tile {
       int va[8];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int row = 64 * s + 16 * t + ln.v_row;
-        const int col = 32 * db + ln.v_col;          // bytes
-        const int off = row * G::ROWB + ((((col >> 4) ^ swz_v<G::CPR, MODE>(row)) << 4) | (col & 15));
-        i32x2 r = lds_tr8(vbase + off);
+        i32x2 r = lds_tr8(vbase + (64 * s + 16 * t) * G::ROWB + ln.vf[db]);
         va[2 * t] = r[0];
         va[2 * t + 1] = r[1];
       }
@@ -445,8 +463,11 @@ struct Tile {
       const int kb = g / 4, i0 = 4 * (g % 4);
       float x0 = st[kb][i0], x1 = st[kb][i0 + 1], x2 = st[kb][i0 + 2], x3 = st[kb][i0 + 3];
       if constexpr (MODE == MODE_FP8) {
-        // step g/8, word g%8 <- scores 4g .. 4g+3 of the tile
-        int word = 0;
+        // step g/8, word g%8 <- scores 4g .. 4g+3 of the tile.  The two
+        // conversions write both halves of the word, so it starts undefined
+        // (a zero start cost a v_mov per word).
+        int word;
+        asm volatile("" : "=v"(word));
         word = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, word, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, word, true);
         pf.f8[g / 8][g % 8] = word;
