@@ -146,7 +146,8 @@ __device__ __forceinline__ int swz_v(int row) {
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ float swap_halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+  // v_maximum_f32: no NaN canonicalisation of the inputs (fmaxf costs two)
+  return __builtin_elementwise_maximum(__int_as_float(r[0]), __int_as_float(r[1]));
 }
 __device__ __forceinline__ float swap_halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
